@@ -1,0 +1,201 @@
+"""Oracle for prefix-reuse ("bipartite") attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never does: it runs
+the HIP library and fails loudly when that library is missing.
+
+The definitions below follow the Bat page ("Bat: Efficient Generative
+Recommender Serving with Bipartite Attention"):
+
+* sections "This paper's idea" and "Why it works" (permutation invariance of
+  user and item tokens): no positional encoding, no causal mask, and either
+  the user history or a set of items may be the cached prefix;
+* sections "Problem" and "Why this problem is worth solving": the prefix's
+  key/value cache is built once and reused across queries;
+* the UG-Separation page's abstract: tokens that stay purely user-side are
+  the reusable ones, hence prefix rows attend within the prefix only;
+* the GBLA page's abstract: encoder attention is bidirectional.
+
+Every function is float64 and plain: the masked attention and the batched
+suffix-row prefill live in ``oracle.c`` (two-pass softmax per row), the rest
+(mask construction, item-prefix gather, paged-pool scatter, log-sum-exp merge)
+is a few lines of numpy each.  Pins: ``tests/test_oracle.py``.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from .build import ensure_built
+
+_lib = None
+
+F32, BF16, F64 = 0, 1, 2
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(ensure_built())
+        p = ctypes.c_void_p
+        i = ctypes.c_int
+        _lib.oracle_attention_masked.argtypes = [i, i, i, i, p, p, p, p,
+                                                 ctypes.c_double, p, p]
+        _lib.oracle_attention_masked.restype = None
+        _lib.oracle_prefill_suffix.argtypes = [i, i, i, i, p, p, p, p, p, p, p,
+                                               ctypes.c_double, i, p, p, p, p]
+        _lib.oracle_prefill_suffix.restype = ctypes.c_int
+        _lib.oracle_num_threads.argtypes = []
+        _lib.oracle_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_input(x):
+    """Return (contiguous array, dtype code).  uint16 arrays are bf16 bits."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, BF16
+    if x.dtype == np.float32:
+        return x, F32
+    return np.ascontiguousarray(x, dtype=np.float64), F64
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def default_scale(D: int) -> float:
+    """Softmax scale 1/sqrt(D), rounded once to float32 (the value both sides use)."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def attention_masked(q, k, v, mask, scale):
+    """Masked softmax attention for one head, float64.
+
+    q [n_q, D], k/v [n_k, D], mask [n_q, n_k] (True = visible).
+    Returns (out [n_q, D] float64, lse [n_q] float64, natural log).
+    """
+    q, dt = _as_input(q)
+    k, dk = _as_input(k)
+    v, dv = _as_input(v)
+    if not (dt == dk == dv):
+        q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
+        dt = F64
+    n_q, D = q.shape
+    n_k = k.shape[0]
+    m = np.ascontiguousarray(mask, dtype=np.uint8).reshape(n_q, n_k)
+    out = np.zeros((n_q, D), np.float64)
+    lse = np.zeros((n_q,), np.float64)
+    _load().oracle_attention_masked(n_q, n_k, D, dt, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(m), float(scale), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def prefix_only_mask(in_prefix):
+    """The bipartite mask over one request's tokens.
+
+    in_prefix[j] is True for prefix tokens.  Query i may see key j iff j is a
+    prefix token, or both i and j are suffix tokens: prefix rows see only the
+    prefix, suffix rows see every token.  Token order plays no role.
+    """
+    p = np.asarray(in_prefix, dtype=bool)
+    return p[None, :] | (~p[:, None] & ~p[None, :])
+
+
+def bipartite_attention(q, k, v, in_prefix, scale):
+    """All rows (prefix and suffix) of one request and head, float64."""
+    return attention_masked(q, k, v, prefix_only_mask(in_prefix), scale)
+
+
+def prefill_suffix(q, k_s, v_s, cu_s, k_p, v_p, cu_p, scale, rows=None,
+                   heads=None):
+    """Batched suffix-row prefill over packed [tokens, H, D] inputs, float64.
+
+    Request r's suffix is rows cu_s[r]:cu_s[r+1] of q/k_s/v_s and its prefix
+    (in the order it sees it) is rows cu_p[r]:cu_p[r+1] of k_p/v_p.  With
+    rows/heads None the result is out [total_s, H, D] and lse [H, total_s];
+    otherwise out [n, D] and lse [n] for the (rows[i], heads[i]) pairs.
+    """
+    q, dt = _as_input(q)
+    arrs = [q]
+    for x in (k_s, v_s, k_p, v_p):
+        x, d2 = _as_input(x)
+        if d2 != dt:
+            raise TypeError("all inputs must share one dtype")
+        arrs.append(x)
+    q, k_s, v_s, k_p, v_p = arrs
+    total_s, H, D = q.shape
+    cu_s = np.ascontiguousarray(cu_s, dtype=np.int32)
+    cu_p = np.ascontiguousarray(cu_p, dtype=np.int32)
+    B = cu_s.shape[0] - 1
+    if cu_p.shape[0] != B + 1 or cu_s[-1] != total_s:
+        raise ValueError("cu_seqlens do not match the packed inputs")
+    if rows is None:
+        n_sel = -1
+        sr = sh = np.zeros(1, np.int32)
+        out = np.zeros((total_s, H, D), np.float64)
+        lse = np.zeros((H, total_s), np.float64)
+    else:
+        sr = np.ascontiguousarray(rows, dtype=np.int32)
+        sh = np.ascontiguousarray(heads, dtype=np.int32)
+        n_sel = sr.shape[0]
+        out = np.zeros((n_sel, D), np.float64)
+        lse = np.zeros((n_sel,), np.float64)
+    rc = _load().oracle_prefill_suffix(B, H, D, dt, _ptr(q), _ptr(k_s), _ptr(v_s),
+                                       _ptr(cu_s), _ptr(k_p), _ptr(v_p), _ptr(cu_p),
+                                       float(scale), n_sel, _ptr(sr), _ptr(sh),
+                                       _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("selected row or head out of range")
+    return out, lse
+
+
+def gather_item_prefix(item_tokens, item_ids, tokens_per_item):
+    """An item-mode prefix: the listed items' tokens, in list order.
+
+    item_tokens is [num_items * tokens_per_item, ...] (item i owns rows
+    i*tpi .. i*tpi+tpi-1); item_ids lists the request's items.
+    """
+    ids = np.asarray(item_ids, dtype=np.int64)
+    rows = (ids[:, None] * tokens_per_item + np.arange(tokens_per_item)[None, :]).reshape(-1)
+    return item_tokens[rows]
+
+
+def kv_scatter(x, cu_lens, block_table, num_blocks, block_size, fill):
+    """The paged pool the prefix build must produce.
+
+    x is packed [tokens, H, D]; token t of request r lands in block
+    block_table[r][t // block_size], slot t % block_size, giving a pool laid
+    out [num_blocks, H, block_size, D].  Slots no token maps to keep `fill`.
+    """
+    x = np.asarray(x)
+    _, H, D = x.shape
+    pool = np.empty((num_blocks, H, block_size, D), dtype=x.dtype)
+    pool[...] = fill
+    bt = np.asarray(block_table)
+    for r in range(len(cu_lens) - 1):
+        for t in range(int(cu_lens[r + 1] - cu_lens[r])):
+            blk = int(bt[r, t // block_size])
+            pool[blk, :, t % block_size, :] = x[cu_lens[r] + t]
+    return pool
+
+
+def lse_merge(parts):
+    """Log-sum-exp merge of attention partials over disjoint key sets.
+
+    parts is a list of (out [..., D], lse [...]) with out normalised over its
+    own keys.  lse = log sum_i exp(lse_i); out = sum_i exp(lse_i - lse) out_i.
+    An empty partial (lse = -inf) contributes nothing.
+    """
+    lses = np.stack([np.asarray(l, np.float64) for _, l in parts])
+    lse = np.logaddexp.reduce(lses, axis=0)
+    out = np.zeros_like(np.asarray(parts[0][0], np.float64))
+    for o, l in parts:
+        w = np.where(np.isneginf(l), 0.0, np.exp(np.asarray(l) - np.where(np.isneginf(lse), 0.0, lse)))
+        out = out + w[..., None] * np.asarray(o, np.float64)
+    return out, lse

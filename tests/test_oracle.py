@@ -1,0 +1,343 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: a hand-worked
+example, an independent brute-force loop, torch's scaled-dot-product
+attention on the CPU, closed forms, invariances and merge identities.  The
+method is the Bat page's prefix-reuse attention (sections "This paper's idea"
+and "Why it works"); the mask reading is prefix rows see only the prefix,
+suffix rows see every token of their request.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from prefix_reuse_attention_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _sym(x):
+    table = {"ln2": math.log(2), "ln3": math.log(3), "ln5": math.log(5),
+             "ln8": math.log(8), "8/3": 8 / 3, "16/3": 16 / 3}
+    if isinstance(x, list):
+        return [_sym(e) for e in x]
+    return table[x] if isinstance(x, str) else float(x)
+
+
+def brute_force(q, k, v, in_prefix, scale):
+    """Independent reference: explicit loops and math.exp, no vectorisation."""
+    n, D = q.shape
+    out = np.zeros((n, D))
+    lse = np.zeros(n)
+    for i in range(n):
+        vis = [j for j in range(n) if in_prefix[j] or (not in_prefix[i] and not in_prefix[j])]
+        s = {j: scale * sum(float(q[i, d]) * float(k[j, d]) for d in range(D)) for j in vis}
+        z = sum(math.exp(s[j]) for j in vis)
+        lse[i] = math.log(z)
+        for j in vis:
+            w = math.exp(s[j]) / z
+            for d in range(D):
+                out[i, d] += w * float(v[j, d])
+    return out, lse
+
+
+def rand_seq(rng, n_p, n_s, D, scale_q=1.0):
+    n = n_p + n_s
+    q = rng.standard_normal((n, D)) * scale_q
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    in_prefix = np.array([True] * n_p + [False] * n_s)
+    return q, k, v, in_prefix
+
+
+# ---------------------------------------------------------------- hand-worked
+def test_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_bipartite.json")))
+    q, k, v = (np.array(_sym(g[x])) for x in ("q", "k", "v"))
+    out, lse = oracle.bipartite_attention(q, k, v, g["in_prefix"], g["scale"])
+    np.testing.assert_allclose(out, np.array(_sym(g["out"])), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(_sym(g["lse"])), rtol=0, atol=1e-12)
+
+
+def test_hand_kv_scatter():
+    g = json.load(open(os.path.join(GOLDEN, "hand_kv_scatter.json")))
+    x = np.array(g["tokens"], dtype=np.int32).reshape(-1, 1, 1)
+    pool = oracle.kv_scatter(x, g["cu_lens"], np.array(g["block_table"]),
+                             g["num_blocks"], g["block_size"], g["fill"])
+    assert pool.shape == (g["num_blocks"], 1, g["block_size"], 1)
+    np.testing.assert_array_equal(pool[:, 0, :, 0], np.array(g["pool"]))
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("n_p", [0, 1, 3, 17])
+@pytest.mark.parametrize("n_s", [1, 2, 5])
+@pytest.mark.parametrize("D", [1, 4, 32])
+def test_brute_force_all_rows(n_p, n_s, D):
+    rng = np.random.default_rng(1000 * n_p + 10 * n_s + D)
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, scale)
+    ref_o, ref_l = brute_force(q, k, v, pre, scale)
+    np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
+
+
+def test_brute_force_config1():
+    """Config 1 (fp32, 4 heads, D=32, 64 prefix + 8 suffix) vs brute force."""
+    wl = W.make_config(1)
+    out, lse = oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, wl.user_k,
+                                     wl.user_v, wl.cu_user, wl.scale)
+    for h in range(wl.H):
+        q = np.concatenate([np.zeros((64, wl.D), np.float32), wl.q[:, h]])
+        k = np.concatenate([wl.user_k[:, h], wl.k_s[:, h]])
+        v = np.concatenate([wl.user_v[:, h], wl.v_s[:, h]])
+        pre = np.array([True] * 64 + [False] * 8)
+        ref_o, ref_l = brute_force(q.astype(np.float64), k.astype(np.float64),
+                                   v.astype(np.float64), pre, wl.scale)
+        np.testing.assert_allclose(out[:, h], ref_o[64:], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h], ref_l[64:], rtol=0, atol=1e-12)
+
+
+def test_prefill_batch_brute_force_and_selection():
+    """Batched suffix rows over several requests (bf16 inputs) vs brute force,
+    and the sampled-row mode returns the same numbers."""
+    wl = W.make_custom(dtype="bf16", H=2, D=8, n_s=[3, 1, 4], n_p=[5, 0, 8],
+                       mode=[W.USER, W.USER, W.ITEM], seed=7, num_items=6)
+    k_p, v_p, cu_p = assemble_prefix(wl)
+    out, lse = oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, wl.scale)
+    qf, ksf, vsf = (W.bf16_to_f32(x).astype(np.float64) for x in (wl.q, wl.k_s, wl.v_s))
+    kpf, vpf = (W.bf16_to_f32(x).astype(np.float64) for x in (k_p, v_p))
+    for r in range(wl.B):
+        s0, s1, p0, p1 = wl.cu_s[r], wl.cu_s[r + 1], cu_p[r], cu_p[r + 1]
+        for h in range(wl.H):
+            q = np.concatenate([np.zeros((p1 - p0, wl.D)), qf[s0:s1, h]])
+            k = np.concatenate([kpf[p0:p1, h], ksf[s0:s1, h]])
+            v = np.concatenate([vpf[p0:p1, h], vsf[s0:s1, h]])
+            pre = np.array([True] * (p1 - p0) + [False] * (s1 - s0))
+            ro, rl = brute_force(q, k, v, pre, wl.scale)
+            np.testing.assert_allclose(out[s0:s1, h], ro[p1 - p0:], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[h, s0:s1], rl[p1 - p0:], rtol=0, atol=1e-12)
+    rows = np.array([0, 3, 7, 5], np.int32)
+    heads = np.array([1, 0, 1, 0], np.int32)
+    so, sl = oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p,
+                                   wl.scale, rows=rows, heads=heads)
+    np.testing.assert_array_equal(so, out[rows, heads])
+    np.testing.assert_array_equal(sl, lse[heads, rows])
+
+
+def assemble_prefix(wl):
+    """Each request's prefix in the order it sees it (item mode: listed items' tokens)."""
+    ks, vs, cu = [], [], [0]
+    for r in range(wl.B):
+        if wl.mode[r] == W.ITEM:
+            ids = wl.block_table[r, : wl.n_p[r] // W.ITEM_TOKENS]
+            ks.append(oracle.gather_item_prefix(wl.item_k, ids, W.ITEM_TOKENS))
+            vs.append(oracle.gather_item_prefix(wl.item_v, ids, W.ITEM_TOKENS))
+        else:
+            ks.append(wl.user_k[wl.cu_user[r]:wl.cu_user[r + 1]])
+            vs.append(wl.user_v[wl.cu_user[r]:wl.cu_user[r + 1]])
+        cu.append(cu[-1] + len(ks[-1]))
+    return np.concatenate(ks), np.concatenate(vs), np.array(cu, np.int32)
+
+
+# ------------------------------------------------------- library routine (SDPA)
+def test_library_sdpa():
+    """Suffix rows equal unmasked SDPA over all tokens; prefix rows equal
+    unmasked SDPA over the prefix alone (torch, float64, CPU)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(3)
+    for n_p, n_s, D in [(0, 4, 16), (9, 5, 16), (33, 7, 64), (64, 8, 32)]:
+        q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+        scale = 1.0 / math.sqrt(D)
+        out, _ = oracle.bipartite_attention(q, k, v, pre, scale)
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None, None]
+        ref_u = F.scaled_dot_product_attention(t(q[n_p:]), t(k), t(v), scale=scale)[0, 0]
+        np.testing.assert_allclose(out[n_p:], ref_u.numpy(), rtol=0, atol=1e-12)
+        if n_p:
+            ref_p = F.scaled_dot_product_attention(t(q[:n_p]), t(k[:n_p]), t(v[:n_p]),
+                                                   scale=scale)[0, 0]
+            np.testing.assert_allclose(out[:n_p], ref_p.numpy(), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+def test_single_token_returns_its_value():
+    rng = np.random.default_rng(0)
+    q, k, v, pre = rand_seq(rng, 0, 1, 8)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.3)
+    np.testing.assert_allclose(out, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.3 * q @ k.T[:, 0], rtol=0, atol=1e-14)
+
+
+def test_constant_values():
+    rng = np.random.default_rng(1)
+    q, k, v, pre = rand_seq(rng, 11, 6, 8)
+    v[:] = np.arange(8) * 0.5 - 1.0
+    out, _ = oracle.bipartite_attention(q, k, v, pre, 0.5)
+    np.testing.assert_allclose(out, np.broadcast_to(v[0], out.shape), rtol=0, atol=1e-13)
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    rng = np.random.default_rng(2)
+    n_p, n_s = 7, 5
+    q, k, v, pre = rand_seq(rng, n_p, n_s, 4)
+    q[:] = 0
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 1.0)
+    np.testing.assert_allclose(out[:n_p], np.broadcast_to(v[:n_p].mean(0), (n_p, 4)), atol=1e-14)
+    np.testing.assert_allclose(out[n_p:], np.broadcast_to(v.mean(0), (n_s, 4)), atol=1e-14)
+    np.testing.assert_allclose(lse[:n_p], math.log(n_p), atol=1e-14)
+    np.testing.assert_allclose(lse[n_p:], math.log(n_p + n_s), atol=1e-14)
+
+
+def test_equal_keys_give_mean_and_log_count():
+    rng = np.random.default_rng(4)
+    n_p, n_s, D = 6, 3, 5
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    k[:] = k[0]
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.7)
+    s = 0.7 * q @ k[0]
+    np.testing.assert_allclose(out[:n_p], np.broadcast_to(v[:n_p].mean(0), (n_p, D)), atol=1e-13)
+    np.testing.assert_allclose(out[n_p:], np.broadcast_to(v.mean(0), (n_s, D)), atol=1e-13)
+    np.testing.assert_allclose(lse[:n_p], s[:n_p] + math.log(n_p), atol=1e-13)
+    np.testing.assert_allclose(lse[n_p:], s[n_p:] + math.log(n_p + n_s), atol=1e-13)
+
+
+def test_dominant_score_selects_its_value():
+    """One score 60 above the rest: weight of the others is below e^-60 * n."""
+    D, n_p, n_s = 4, 5, 3
+    q = np.zeros((n_p + n_s, D)); q[:, 0] = 1.0
+    k = np.zeros((n_p + n_s, D)); k[2, 0] = 60.0          # prefix token 2 dominates
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((n_p + n_s, D))
+    pre = np.array([True] * n_p + [False] * n_s)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 1.0)
+    np.testing.assert_allclose(out, np.broadcast_to(v[2], out.shape), rtol=0, atol=1e-24 * 10)
+    np.testing.assert_allclose(lse[n_p:], 60.0 + math.log1p((n_p + n_s - 1) * math.exp(-60)), atol=1e-13)
+
+
+def test_duplicate_key_equals_ln2_shift():
+    """A (k, v) pair present twice weighs as if its score were raised by ln 2."""
+    rng = np.random.default_rng(6)
+    D = 6
+    q0 = rng.standard_normal(D)
+    ks = rng.standard_normal((4, D)); vs = rng.standard_normal((4, D))
+    scale = 0.4
+    # duplicated key 1
+    k_dup = np.vstack([ks, ks[1:2]]); v_dup = np.vstack([vs, vs[1:2]])
+    o1, l1 = oracle.attention_masked(q0[None], k_dup, v_dup, np.ones((1, 5)), scale)
+    # key 1 moved along q so that its score grows by exactly ln 2
+    k_sh = ks.copy(); k_sh[1] += (math.log(2) / scale) * q0 / (q0 @ q0)
+    o2, l2 = oracle.attention_masked(q0[None], k_sh, vs, np.ones((1, 4)), scale)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- invariances
+def test_permuting_prefix_leaves_suffix_rows():
+    rng = np.random.default_rng(8)
+    n_p, n_s, D = 13, 6, 16
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.25)
+    perm = np.concatenate([rng.permutation(n_p), np.arange(n_p, n_p + n_s)])
+    o2, l2 = oracle.bipartite_attention(q[perm], k[perm], v[perm], pre, 0.25)
+    np.testing.assert_allclose(o2[n_p:], out[n_p:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o2[:n_p], out[perm[:n_p]], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, lse[perm], rtol=0, atol=1e-13)
+
+
+def test_permuting_suffix_permutes_rows():
+    rng = np.random.default_rng(9)
+    n_p, n_s, D = 10, 7, 8
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.3)
+    perm = np.concatenate([np.arange(n_p), n_p + rng.permutation(n_s)])
+    o2, l2 = oracle.bipartite_attention(q[perm], k[perm], v[perm], pre, 0.3)
+    np.testing.assert_allclose(o2, out[perm], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, lse[perm], rtol=0, atol=1e-13)
+
+
+def test_group_order_is_irrelevant():
+    """[P; U] and [U; P] (mask carried by membership, not position) agree, and
+    so does any interleaving: the order-agnostic view of user and item tokens."""
+    rng = np.random.default_rng(10)
+    n_p, n_s, D = 9, 5, 8
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.35)
+    for perm in (np.concatenate([np.arange(n_p, n_p + n_s), np.arange(n_p)]),
+                 rng.permutation(n_p + n_s)):
+        o2, l2 = oracle.bipartite_attention(q[perm], k[perm], v[perm], pre[perm], 0.35)
+        np.testing.assert_allclose(o2, out[perm], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l2, lse[perm], rtol=0, atol=1e-13)
+
+
+def test_item_order_in_block_table_is_irrelevant():
+    wl = W.make_custom(dtype="bf16", H=2, D=16, n_s=[5, 3], n_p=[24, 12],
+                       mode=[W.ITEM, W.ITEM], seed=11, num_items=40)
+    k_p, v_p, cu_p = assemble_prefix(wl)
+    out, lse = oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, wl.scale)
+    rng = np.random.default_rng(12)
+    for r in range(wl.B):
+        n = wl.n_p[r] // W.ITEM_TOKENS
+        wl.block_table[r, :n] = wl.block_table[r, rng.permutation(n)]
+    k2, v2, cu2 = assemble_prefix(wl)
+    o2, l2 = oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k2, v2, cu2, wl.scale)
+    np.testing.assert_allclose(o2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, lse, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------- merge identities
+def _partial(q, k, v, rows, keys, scale):
+    mask = np.zeros((len(q), len(k)), bool)
+    mask[np.ix_(rows, keys)] = True
+    o, l = oracle.attention_masked(q, k, v, mask, scale)
+    return o[rows], l[rows]
+
+
+def test_merge_of_prefix_and_suffix_partials_is_full():
+    rng = np.random.default_rng(13)
+    n_p, n_s, D = 21, 9, 16
+    q, k, v, pre = rand_seq(rng, n_p, n_s, D)
+    out, lse = oracle.bipartite_attention(q, k, v, pre, 0.25)
+    U = np.arange(n_p, n_p + n_s)
+    pp = _partial(q, k, v, U, np.arange(n_p), 0.25)
+    pu = _partial(q, k, v, U, U, 0.25)
+    mo, ml = oracle.lse_merge([pp, pu])
+    np.testing.assert_allclose(mo, out[U], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ml, lse[U], rtol=0, atol=1e-13)
+    # commutative
+    mo2, ml2 = oracle.lse_merge([pu, pp])
+    np.testing.assert_allclose(mo2, mo, rtol=0, atol=1e-14)
+    # any chunking of the prefix, merged in any grouping
+    cuts = [0, 4, 5, 13, n_p]
+    chunks = [_partial(q, k, v, U, np.arange(a, b), 0.25) for a, b in zip(cuts, cuts[1:])]
+    left = oracle.lse_merge([oracle.lse_merge(chunks[:2]), oracle.lse_merge(chunks[2:] + [pu])])
+    np.testing.assert_allclose(left[0], out[U], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(left[1], lse[U], rtol=0, atol=1e-13)
+
+
+def test_merge_with_empty_partial_is_identity():
+    rng = np.random.default_rng(14)
+    q, k, v, pre = rand_seq(rng, 0, 6, 8)
+    U = np.arange(6)
+    pu = _partial(q, k, v, U, U, 0.5)
+    empty = _partial(q, k, v, U, np.array([], int), 0.5)
+    assert np.all(np.isneginf(empty[1])) and np.all(empty[0] == 0)
+    mo, ml = oracle.lse_merge([empty, pu])
+    np.testing.assert_array_equal(ml, pu[1])
+    np.testing.assert_allclose(mo, pu[0], rtol=0, atol=0)
+
+
+def test_planted_mistake_is_caught():
+    """A plausible oracle bug (prefix rows allowed to see the suffix) changes
+    the prefix rows enough for the brute-force pin to fail."""
+    rng = np.random.default_rng(15)
+    q, k, v, pre = rand_seq(rng, 5, 4, 8)
+    good, _ = oracle.bipartite_attention(q, k, v, pre, 0.35)
+    wrong, _ = oracle.attention_masked(q, k, v, np.ones((9, 9)), 0.35)
+    ref, _ = brute_force(q, k, v, pre, 0.35)
+    assert np.abs(wrong[:5] - ref[:5]).max() > 1e-3
+    np.testing.assert_allclose(good, ref, atol=1e-12)

@@ -1,0 +1,226 @@
+"""Benchmark of prefix-reuse prefill attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+
+One step is one bat_attn_prefill call over the whole batch (device work
+decomposition + attention with the prefix gathered from the paged cache +
+any split merge), inputs and the prefix pool already resident in HBM.  The
+prefix build (bat_kv_build) is the once-per-prefix cost that reuse amortises;
+it is timed separately and reported beside the step.  Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_d128_config4_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "prefix_reuse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, per_launch_units):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_hash") != kernel_source_hash() or s.get("config") != config:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request with no exchange; see the design notes)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd import workloads as W
+    from prefix_reuse_attention_amd.device import DeviceWorkload
+
+    api.load()  # the HIP library must be there: no fallback
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    t0 = time.time()
+    wl = W.make_config(args.config)
+    print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",
+          file=sys.stderr, flush=True)
+
+    dw = DeviceWorkload(wl, build=False)
+    stream = torch.cuda.current_stream()
+    # ---- prefix build (amortised over reuse), timed on its own
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dw.upload_prefix()
+    dw.alloc_pools()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    dw.build_kv()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    build_bytes = dw.prefix_bytes()
+    dw.drop_prefix_source()
+    ws = dw.workspace()
+    out = torch.empty_like(dw.q)
+    lse = torch.empty((wl.H, wl.total_s), dtype=torch.float32, device="cuda")
+
+    def step():
+        dw.run(out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    per_call_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall_s * 1e3 / args.steps
+    flops = wl.flops()
+    alg_bytes = wl.alg_bytes()
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    tok_s = wl.total_s / (ms_per_step * 1e-3)
+    kernel_ms = float(per_call_ms.mean())
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    bf16 = wl.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    traffic = measured_traffic(wl.name, 1)
+    props = torch.cuda.get_device_properties(0)
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events: mean "
+          f"{kernel_ms:.4f}, min {per_call_ms.min():.4f}, p90 {np.percentile(per_call_ms, 90):.4f})"
+          f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = run_cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak) + suffix tokens/s, 1 GPU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, shuffled paged prefix pool)",
+        "config": {"workload": f"{wl.name}: {wl.notes['description']}", "B": wl.B, "H": wl.H,
+                   "D": wl.D, "total_suffix": wl.total_s, "total_prefix": int(wl.n_p.sum()),
+                   "user_block_size": wl.user_block_size, "seed": wl.seed},
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2) if bf16 else None,
+        "suffix_tokens_per_s": round(tok_s, 1),
+        "alg_flops_per_step": flops,
+        "alg_bytes_per_step": alg_bytes,
+        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_bf16_kernel<128>" if (bf16 and wl.D == 128) else
+                               ("attn_bf16_kernel<64>" if bf16 else f"attn_f32_kernel<{wl.D}>"),
+                     "kernel_ms_mean": round(kernel_ms, 5)},
+        "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
+                     "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),
+                     "note": "once per prefix; amortised over every query that reuses it"},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_cpu_baseline(wl, target_s):
+    """The oracle (float64, OpenMP) on a bounded random sample of (suffix row,
+    head) pairs of the same workload, scaled to TFLOP/s of algorithmic work."""
+    import numpy as np
+    import oracle
+    from prefix_reuse_attention_amd import workloads as W
+
+    rng = np.random.default_rng(12345)
+
+    def sample(n):
+        rows = rng.integers(0, wl.total_s, size=n).astype(np.int32)
+        heads = rng.integers(0, wl.H, size=n).astype(np.int32)
+        return rows, heads
+
+    # each request's prefix as the oracle sees it (contiguous, block-table order)
+    ks, vs, cu = [], [], [0]
+    for r in range(wl.B):
+        if wl.mode[r] == W.ITEM:
+            ids = wl.block_table[r, : wl.n_p[r] // W.ITEM_TOKENS]
+            ks.append(oracle.gather_item_prefix(wl.item_k, ids, W.ITEM_TOKENS))
+            vs.append(oracle.gather_item_prefix(wl.item_v, ids, W.ITEM_TOKENS))
+        else:
+            ks.append(wl.user_k[wl.cu_user[r]:wl.cu_user[r + 1]])
+            vs.append(wl.user_v[wl.cu_user[r]:wl.cu_user[r + 1]])
+        cu.append(cu[-1] + len(ks[-1]))
+    k_p, v_p = np.concatenate(ks), np.concatenate(vs)
+    cu_p = np.array(cu, np.int32)
+    del ks, vs
+
+    def pair_flops(rows):
+        req = np.searchsorted(wl.cu_s, rows, side="right") - 1
+        return float(np.sum(4.0 * wl.D * (wl.n_p[req] + wl.n_s[req])))
+
+    n = 64
+    while True:
+        rows, heads = sample(n)
+        t = time.perf_counter()
+        oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, wl.scale,
+                              rows=rows, heads=heads)
+        dt = time.perf_counter() - t
+        if dt >= target_s / 4 or n >= wl.total_s * wl.H:
+            break
+        n = int(min(wl.total_s * wl.H, max(2 * n, n * (target_s / 2) / max(dt, 1e-3))))
+    rows, heads = sample(max(1, int(n * target_s / max(dt, 1e-6))))
+    t = time.perf_counter()
+    oracle.prefill_suffix(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, wl.scale,
+                          rows=rows, heads=heads)
+    dt = time.perf_counter() - t
+    fl = pair_flops(rows)
+    print(f"[bench] oracle baseline: {len(rows)} (row, head) pairs in {dt:.1f}s",
+          file=sys.stderr, flush=True)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} random (suffix row, head) pairs of {wl.name}, float64, "
+                      f"{dt:.1f} s; rate = algorithmic flops of those pairs / time",
+            "suffix_tokens_per_s_equiv": round(len(rows) / wl.H / dt, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * bat.h -- C ABI of the MI355X (gfx950) prefix-reuse ("bipartite") attention
+ * library, libbat.so.
+ *
+ * The method is the one the Bat page ("Bat: Efficient Generative Recommender
+ * Serving with Bipartite Attention") describes: user and item tokens are
+ * order-agnostic, so either group may be the prompt prefix whose key/value
+ * cache is built once and reused (sections "This paper's idea", "Why it
+ * works"), and user-prefix and item-prefix caches live in separate pools
+ * (section "Why it works", the disaggregated cache pool).  This library is
+ * the data-parallel hot path of that method on one GPU: building the paged
+ * prefix cache, and prefill attention of the fresh (suffix) tokens over the
+ * cached prefix plus their own group.
+ *
+ * Attention semantics (identical in both prefix modes): scaled dot-product
+ * softmax, no positional encoding, no causal mask.  For request r and head h
+ * with prefix tokens P and suffix tokens U, a suffix row i sees every token
+ * of P and U:
+ *     S_ij = softmax_scale * <q_i, k_j>
+ *     lse_i = ln sum_j exp(S_ij),   out_i = sum_j exp(S_ij - lse_i) v_j.
+ * (Prefix rows would see P only; their outputs are what was cached and are
+ * not recomputed here.)
+ *
+ * Conventions for every entry point
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device or host memory and keeps no state between calls; scratch space
+ *     is the caller's workspace.
+ *   - Pointers named "device" must be device (HBM) pointers; host scalars are
+ *     passed by value.  `stream` is a hipStream_t (NULL = the null stream);
+ *     all work is enqueued asynchronously on it.
+ *   - Layouts are row-major.  "Packed" activations are token-major
+ *     [tokens, H, D] with a cumulative-length array cu_* of B+1 int32
+ *     (cu[0] = 0, cu[r+1] - cu[r] = tokens of request r).
+ *   - Errors: a bat_status is returned; nothing is thrown across the ABI.
+ *     Host-detectable argument errors return before anything is enqueued.
+ *     With the environment variable BAT_VALIDATE=1 the library also checks
+ *     block ids and lengths on the device, synchronises the stream and
+ *     returns BAT_ERR_BLOCK_TABLE on a violation.  Without it, an
+ *     out-of-range block id is never dereferenced (the kernels treat its
+ *     tokens as zero keys/values, or skip the write) but the result is
+ *     unspecified.
+ *   - Thread safety: calls are independent; concurrent calls must not share
+ *     a workspace.
+ */
+#ifndef BAT_H_
+#define BAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bat_status {
+  BAT_OK = 0,
+  BAT_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size */
+  BAT_ERR_UNSUPPORTED = 2, /* no kernel for this (dtype, head_dim) */
+  BAT_ERR_BLOCK_TABLE = 3, /* device validation: bad block id or length */
+  BAT_ERR_WORKSPACE = 4,   /* workspace NULL or too small */
+  BAT_ERR_HIP = 5          /* a HIP runtime call or launch failed */
+} bat_status;
+
+typedef enum bat_dtype {
+  BAT_F32 = 0,  /* float32 in, float32 out, float32 arithmetic */
+  BAT_BF16 = 1  /* bfloat16 in/out, float32 accumulation */
+} bat_dtype;
+
+/* Which pool a request's prefix comes from (one byte per request). */
+typedef enum bat_prefix_mode {
+  BAT_PREFIX_USER = 0, /* the user's history, paged in the user pool */
+  BAT_PREFIX_ITEM = 1  /* cached items, one item per item-pool block */
+} bat_prefix_mode;
+
+/*
+ * A paged key/value pool (the disaggregated cache pool of the Bat page,
+ * section "Why it works": user-prefix and item-prefix caches are separate
+ * pools).  k and v are device buffers laid out [num_blocks, H, block_size, D]
+ * in the dtype of the call.  Token t of a prefix lives in block
+ * block_table[t / block_size], slot t % block_size.  block_size is a power
+ * of two in [1, 256].  An item pool holds one item per block, so an item id
+ * is its block id and block_size is the item's token count (4 here).
+ */
+typedef struct bat_kv_pool {
+  void *k;
+  void *v;
+  int32_t num_blocks;
+  int32_t block_size;
+} bat_kv_pool;
+
+/*
+ * bat_kv_build -- write prefix keys and values into a paged pool.
+ *
+ * Builds the reusable prefix cache that later prefills read (Bat page,
+ * sections "Problem" and "Why this problem is worth solving": the prefix's
+ * key/value cache is computed once and reused).  A bit-exact copy: token t
+ * of request r, head h goes to pool->k/v[block_table[r*bt_stride + t/bs],
+ * h, t % bs, :].
+ *
+ *   k, v          device, packed [total_tokens, H, D], dtype dt
+ *   cu_lens       device int32 [B+1]; cu_lens[B] must equal total_tokens
+ *   block_table   device int32 [B, bt_stride]; only the first
+ *                 ceil(len_r / bs) entries of row r are read
+ *   B, H, D       requests (or items), heads, head dim (D in {32, 64, 128})
+ *   total_tokens  host copy of cu_lens[B] (sizes the launch); 0 is a no-op
+ *   pool          host pointer to the destination pool description
+ * Slots that no token maps to are left untouched.  Ids outside
+ * [0, num_blocks) are skipped (and reported under BAT_VALIDATE=1).
+ */
+bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
+                        const int32_t *block_table, int32_t bt_stride,
+                        int32_t B, int32_t H, int32_t D, int32_t total_tokens,
+                        bat_dtype dt, const bat_kv_pool *pool, void *stream);
+
+/*
+ * bat_attn_workspace_size -- bytes of device workspace bat_attn_prefill needs
+ * for these host-side bounds (work list, per-request metadata, and the
+ * partial results of prefixes split across workgroups).  Returns 0 for
+ * invalid arguments.
+ */
+size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
+                               int32_t total_suffix, int32_t max_suffix_len,
+                               int32_t max_prefix_len);
+
+/*
+ * bat_attn_prefill -- prefill attention of the suffix rows over the cached
+ * prefix and their own group (the Bipartite Attention of the Bat page,
+ * section "This paper's idea": either the user history or a set of cached
+ * items is the prefix; the suffix is computed fresh).
+ *
+ *   q, k, v         device, packed fresh suffix [total_suffix, H, D], dtype dt
+ *   cu_suffix_lens  device int32 [B+1]
+ *   prefix_lens     device int32 [B]; prefix tokens of each request (0 ok).
+ *                   An item-mode prefix has block_size tokens per listed item.
+ *   prefix_mode     device uint8 [B], bat_prefix_mode per request
+ *   block_table     device int32 [B, bt_stride]: user-mode rows list user-pool
+ *                   blocks, item-mode rows list item ids (item-pool blocks),
+ *                   in the order the request sees them
+ *   user_pool, item_pool  host pointers; either may be NULL if no request
+ *                   uses it
+ *   softmax_scale   multiplies q.k (pass 1/sqrt(D) for standard attention)
+ *   total_suffix    host copy of cu_suffix_lens[B]
+ *   max_suffix_len, max_prefix_len  host upper bounds over requests
+ *   out             device [total_suffix, H, D], dtype dt
+ *   lse             device float32 [H, total_suffix] (natural log), or NULL
+ *   workspace       device, >= bat_attn_workspace_size(...) bytes
+ * Supported: BAT_BF16 with D in {64, 128}; BAT_F32 with D in {32, 64, 128}.
+ * Requests with no suffix tokens write nothing.  The result does not depend
+ * on the physical placement of blocks: the reduction order depends only on
+ * logical lengths.
+ */
+bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_suffix_lens,
+                            const int32_t *prefix_lens,
+                            const uint8_t *prefix_mode,
+                            const int32_t *block_table, int32_t bt_stride,
+                            const bat_kv_pool *user_pool,
+                            const bat_kv_pool *item_pool, int32_t B, int32_t H,
+                            int32_t D, bat_dtype dt, float softmax_scale,
+                            int32_t total_suffix, int32_t max_suffix_len,
+                            int32_t max_prefix_len, void *out, float *lse,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * bat_lse_merge -- combine n_parts attention partials over disjoint key sets
+ * into one result (the log-sum-exp merge; it is how a prefix split across
+ * workgroups, or across devices, is recombined, and it is exact: merging the
+ * prefix partial with the suffix partial gives the same rows as attending to
+ * both at once).
+ *
+ *   o_parts    device float32 [n_parts, rows, H, D], each part normalised
+ *              over its own keys
+ *   lse_parts  device float32 [n_parts, H, rows], natural log; -inf marks an
+ *              empty part (contributes nothing)
+ *   out        device [rows, H, D] in dtype dt
+ *   lse        device float32 [H, rows] or NULL
+ * lse = ln sum_p exp(lse_p); out = sum_p exp(lse_p - lse) o_p.
+ */
+bat_status bat_lse_merge(const float *o_parts, const float *lse_parts,
+                         int32_t n_parts, int32_t rows, int32_t H, int32_t D,
+                         bat_dtype dt, void *out, float *lse, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *bat_status_string(bat_status s);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int32_t bat_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAT_H_ */

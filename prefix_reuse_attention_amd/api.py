@@ -1,0 +1,220 @@
+"""Thin torch-tensor binding over libbat's C ABI (include/bat.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, status codes become exceptions.  Every step of
+the computation runs in the HIP kernels; there is no fallback, and a missing
+library raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbat.so")
+
+BAT_OK, BAT_ERR_INVALID_ARG, BAT_ERR_UNSUPPORTED, BAT_ERR_BLOCK_TABLE, BAT_ERR_WORKSPACE, \
+    BAT_ERR_HIP = range(6)
+BAT_F32, BAT_BF16 = 0, 1
+BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
+
+EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill", "bat_lse_merge",
+            "bat_status_string", "bat_version")
+
+_lib = None
+
+
+class BatError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class KvPool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+
+
+def load():
+    """Load libbat.so (built by prefix_reuse_attention_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libbat.so is not built ({LIB_PATH}); run "
+                           "`python -m prefix_reuse_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    PP = ctypes.POINTER(KvPool)
+    lib.bat_kv_build.argtypes = [P, P, P, P, I, I, I, I, I, I, PP, P]
+    lib.bat_kv_build.restype = I
+    lib.bat_attn_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.bat_attn_workspace_size.restype = ctypes.c_size_t
+    lib.bat_attn_prefill.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I, I,
+                                     P, P, P, ctypes.c_size_t, P]
+    lib.bat_attn_prefill.restype = I
+    lib.bat_lse_merge.argtypes = [P, P, I, I, I, I, I, P, P, P]
+    lib.bat_lse_merge.restype = I
+    lib.bat_status_string.argtypes = [I]
+    lib.bat_status_string.restype = ctypes.c_char_p
+    lib.bat_version.argtypes = []
+    lib.bat_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().bat_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load().bat_version()
+
+
+def _check(status, where):
+    if status != BAT_OK:
+        raise BatError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BAT_BF16
+    if t.dtype == torch.float32:
+        return BAT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class Pool:
+    """A paged K/V pool: k and v are [num_blocks, H, block_size, D] device tensors."""
+    k: object
+    v: object
+    block_size: int
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k.shape[0])
+
+    def struct(self):
+        return KvPool(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.block_size)
+
+
+def new_pool(num_blocks, H, block_size, D, dtype, fill=None):
+    torch = _torch()
+    k = torch.empty((num_blocks, H, block_size, D), dtype=dtype, device="cuda")
+    v = torch.empty_like(k)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return Pool(k, v, block_size)
+
+
+def kv_build(k, v, cu_lens, block_table, pool: Pool):
+    """Scatter packed prefix K/V [tokens, H, D] into `pool` through block_table."""
+    torch = _torch()
+    _need(k, "k"); _need(v, "v", k.dtype)
+    _need(cu_lens, "cu_lens", torch.int32); _need(block_table, "block_table", torch.int32)
+    _need(pool.k, "pool.k", k.dtype); _need(pool.v, "pool.v", k.dtype)
+    total, H, D = k.shape
+    B = cu_lens.shape[0] - 1
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, stride]")
+    ps = pool.struct()
+    st = load().bat_kv_build(_ptr(k), _ptr(v), _ptr(cu_lens), _ptr(block_table),
+                             block_table.shape[1], B, H, D, total, _dtype_code(k),
+                             ctypes.byref(ps), _stream())
+    _check(st, "bat_kv_build")
+
+
+def workspace_size(B, H, D, dtype_code, total_suffix, max_suffix_len, max_prefix_len) -> int:
+    return int(load().bat_attn_workspace_size(B, H, D, dtype_code, total_suffix,
+                                              max_suffix_len, max_prefix_len))
+
+
+def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
+                 user_pool=None, item_pool=None, softmax_scale=None, max_suffix_len=None,
+                 max_prefix_len=None, out=None, lse=None, workspace=None, want_lse=False):
+    """Suffix-row prefill over the cached prefix and the suffix itself.
+
+    q/k/v: packed [total_suffix, H, D] (bf16 or fp32).  Returns (out, lse);
+    lse is [H, total_suffix] float32 or None.  max_*_len are host-side upper
+    bounds over the batch (pass them to avoid a device-to-host read).
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(cu_suffix_lens, "cu_suffix_lens", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    _need(prefix_mode, "prefix_mode", torch.uint8)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32)
+    total, H, D = q.shape
+    B = cu_suffix_lens.shape[0] - 1
+    if max_suffix_len is None:
+        max_suffix_len = int((cu_suffix_lens[1:] - cu_suffix_lens[:-1]).max().item()) if B else 0
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_lens.max().item()) if B else 0
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    ws_bytes = workspace_size(B, H, D, dt, total, max_suffix_len, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    up = user_pool.struct() if user_pool is not None else None
+    ip = item_pool.struct() if item_pool is not None else None
+    if up is not None:
+        _need(user_pool.k, "user_pool.k", q.dtype)
+    if ip is not None:
+        _need(item_pool.k, "item_pool.k", q.dtype)
+    st = load().bat_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_suffix_lens), _ptr(prefix_lens), _ptr(prefix_mode),
+        _ptr(block_table), 0 if block_table is None else block_table.shape[1],
+        ctypes.byref(up) if up is not None else None,
+        ctypes.byref(ip) if ip is not None else None,
+        B, H, D, dt, float(softmax_scale), total, int(max_suffix_len), int(max_prefix_len),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "bat_attn_prefill")
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out_dtype, out=None, lse=None, want_lse=True):
+    """Merge partials o_parts [n, rows, H, D] fp32 / lse_parts [n, H, rows] fp32."""
+    torch = _torch()
+    _need(o_parts, "o_parts", torch.float32)
+    _need(lse_parts, "lse_parts", torch.float32)
+    n, rows, H, D = o_parts.shape
+    if out is None:
+        out = torch.empty((rows, H, D), dtype=out_dtype, device=o_parts.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, rows), dtype=torch.float32, device=o_parts.device)
+    st = load().bat_lse_merge(_ptr(o_parts), _ptr(lse_parts), n, rows, H, D,
+                              _dtype_code(out), _ptr(out), _ptr(lse), _stream())
+    _check(st, "bat_lse_merge")
+    return out, lse

@@ -1,0 +1,281 @@
+// C ABI of libbat: argument validation, workspace layout, kernel dispatch.
+// Every launch goes on the caller's stream; nothing here allocates memory.
+#include <cstdlib>
+#include <cstring>
+
+#include "common.h"
+
+namespace bat {
+hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu, const int32_t *bt,
+                           int32_t bt_stride, int32_t B, int32_t H, int32_t D, int32_t total,
+                           int elem_bytes, void *pk, void *pv, int32_t num_blocks,
+                           int32_t bs_log2, int32_t *err, hipStream_t stream);
+hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B, int32_t H,
+                       int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
+                       int32_t *req_key,
+                       int32_t *req_order, ReqMeta *meta, WorkItem *items, int32_t *hdr,
+                       hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams &p, int D, int grid, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
+hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream);
+hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
+                            int H, int D, bool bf16, void *out, float *lse, hipStream_t stream);
+int bf16_rows_per_item(int D);
+int bf16_keys_per_tile(int D);
+int f32_rows_per_item();
+int f32_keys_per_tile();
+
+// Error word of bat_kv_build under BAT_VALIDATE (one per device).
+__device__ int32_t g_kv_build_err;
+
+__global__ void clear_word_kernel(int32_t *w) { *w = 0; }
+
+namespace {
+
+bool validate_enabled() {
+  const char *e = std::getenv("BAT_VALIDATE");
+  return e && e[0] && std::strcmp(e, "0") != 0;
+}
+
+int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+bool supported(bat_dtype dt, int D) {
+  if (dt == BAT_BF16) return D == 64 || D == 128;
+  if (dt == BAT_F32) return D == 32 || D == 64 || D == 128;
+  return false;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The decomposition policy: rows per item, keys per tile, prefix chunking.
+// A pure function of host-side bounds so that the workspace size and the
+// launch agree.
+struct Plan {
+  int bm = 0, bn = 0;
+  int chunk_len = 0;      // 0: prefixes are never split
+  int max_chunks = 1;
+  int64_t grid = 0;       // work-item slots (upper bound, multiple of 8)
+  int64_t part_rows = 0;  // split partial rows
+  size_t off_items = 0, off_meta = 0, off_key = 0, off_order = 0, off_part_o = 0,
+         off_part_lse = 0, total = 0;
+};
+
+bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
+               int32_t max_p, Plan &pl) {
+  if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
+  if (!supported(dt, D)) return false;
+  pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(D) : f32_rows_per_item();
+  pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D) : f32_keys_per_tile();
+  // Split a prefix only when the unsplit batch cannot fill the GPU
+  // (about two items per CU on 256 CUs) and the prefix is long.
+  const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
+  const int64_t target = 512;
+  pl.chunk_len = 0;
+  if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
+    const int v = std::atoi(e);
+    if (v > 0) pl.chunk_len = ((v + pl.bn - 1) / pl.bn) * pl.bn;
+  } else if (lower_items > 0 && lower_items < target && max_p >= 2048) {
+    int64_t c = (target + lower_items - 1) / lower_items;
+    if (c > 64) c = 64;
+    int64_t len = (max_p + c - 1) / c;
+    if (len < 512) len = 512;
+    pl.chunk_len = (int)(((len + pl.bn - 1) / pl.bn) * pl.bn);
+  }
+  pl.max_chunks = (pl.chunk_len > 0 && max_p > pl.chunk_len)
+                      ? (max_p + pl.chunk_len - 1) / pl.chunk_len : 1;
+  const int64_t t_max = (max_s + pl.bm - 1) / pl.bm;
+  const int64_t n_groups = (int64_t)H * B * pl.max_chunks;
+  pl.grid = kNumXcd * ((n_groups + kNumXcd - 1) / kNumXcd) * t_max;
+  pl.part_rows = pl.max_chunks > 1 ? (int64_t)pl.max_chunks * total_s : 0;
+  if (pl.grid > (int64_t)1 << 30) return false;
+  size_t off = align256(kHdrWords * sizeof(int32_t));
+  pl.off_items = off;    off = align256(off + sizeof(WorkItem) * (size_t)pl.grid);
+  pl.off_meta = off;     off = align256(off + sizeof(ReqMeta) * (size_t)B);
+  pl.off_key = off;      off = align256(off + sizeof(int32_t) * (size_t)B);
+  pl.off_order = off;    off = align256(off + sizeof(int32_t) * (size_t)B);
+  pl.off_part_o = off;   off = align256(off + sizeof(float) * (size_t)pl.part_rows * H * D);
+  pl.off_part_lse = off; off = align256(off + sizeof(float) * (size_t)pl.part_rows * H);
+  pl.total = off;
+  return true;
+}
+
+bat_status pool_desc(const bat_kv_pool *pool, const void *&k, const void *&v, int32_t &blocks,
+                     int32_t &lg) {
+  if (!pool) {
+    k = v = nullptr;
+    blocks = 0;
+    lg = 0;
+    return BAT_OK;
+  }
+  lg = log2_exact(pool->block_size);
+  if (lg < 0 || pool->block_size > 256 || pool->num_blocks < 0) return BAT_ERR_INVALID_ARG;
+  if (pool->num_blocks > 0 && (!pool->k || !pool->v)) return BAT_ERR_INVALID_ARG;
+  k = pool->k;
+  v = pool->v;
+  blocks = pool->num_blocks;
+  return BAT_OK;
+}
+
+}  // namespace
+}  // namespace bat
+
+using namespace bat;
+
+extern "C" {
+
+const char *bat_status_string(bat_status s) {
+  switch (s) {
+    case BAT_OK: return "BAT_OK";
+    case BAT_ERR_INVALID_ARG: return "BAT_ERR_INVALID_ARG: null pointer or invalid size";
+    case BAT_ERR_UNSUPPORTED: return "BAT_ERR_UNSUPPORTED: no kernel for this dtype/head_dim";
+    case BAT_ERR_BLOCK_TABLE: return "BAT_ERR_BLOCK_TABLE: block id or length out of range";
+    case BAT_ERR_WORKSPACE: return "BAT_ERR_WORKSPACE: workspace missing or too small";
+    case BAT_ERR_HIP: return "BAT_ERR_HIP: HIP runtime or launch error";
+  }
+  return "unknown bat_status";
+}
+
+int32_t bat_version(void) { return 100; }
+
+bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
+                        const int32_t *block_table, int32_t bt_stride, int32_t B, int32_t H,
+                        int32_t D, int32_t total_tokens, bat_dtype dt, const bat_kv_pool *pool,
+                        void *stream) {
+  if (!pool || B < 0 || H <= 0 || total_tokens < 0 || bt_stride < 0) return BAT_ERR_INVALID_ARG;
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (!(D == 32 || D == 64 || D == 128)) return BAT_ERR_UNSUPPORTED;
+  const int lg = log2_exact(pool->block_size);
+  if (lg < 0 || pool->block_size > 256 || pool->num_blocks < 0) return BAT_ERR_INVALID_ARG;
+  if (total_tokens == 0) return BAT_OK;
+  if (B == 0 || bt_stride == 0) return BAT_ERR_INVALID_ARG;
+  if (!k || !v || !cu_lens || !block_table || !pool->k || !pool->v) return BAT_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const bool val = validate_enabled();
+  int32_t *err = nullptr;
+  if (val) {
+    if (hipGetSymbolAddress((void **)&err, HIP_SYMBOL(g_kv_build_err)) != hipSuccess)
+      return BAT_ERR_HIP;
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, err);
+  }
+  const int eb = dt == BAT_BF16 ? 2 : 4;
+  if (launch_kv_build(k, v, cu_lens, block_table, bt_stride, B, H, D, total_tokens, eb, pool->k,
+                      pool->v, pool->num_blocks, lg, err, st) != hipSuccess)
+    return BAT_ERR_HIP;
+  if (val) {
+    int32_t h_err = 0;
+    if (hipMemcpyAsync(&h_err, err, sizeof h_err, hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return BAT_ERR_HIP;
+    if (h_err) return BAT_ERR_BLOCK_TABLE;
+  }
+  return BAT_OK;
+}
+
+size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
+                               int32_t total_suffix, int32_t max_suffix_len,
+                               int32_t max_prefix_len) {
+  Plan pl;
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl)) return 0;
+  return pl.total;
+}
+
+bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                            const uint8_t *prefix_mode, const int32_t *block_table,
+                            int32_t bt_stride, const bat_kv_pool *user_pool,
+                            const bat_kv_pool *item_pool, int32_t B, int32_t H, int32_t D,
+                            bat_dtype dt, float softmax_scale, int32_t total_suffix,
+                            int32_t max_suffix_len, int32_t max_prefix_len, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
+      bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
+  AttnParams p{};
+  for (int i = 0; i < 2; ++i) {
+    const bat_status s = pool_desc(i == 0 ? user_pool : item_pool, p.pool_k[i], p.pool_v[i],
+                                   p.pool_blocks[i], p.pool_bs_log2[i]);
+    if (s != BAT_OK) return s;
+  }
+  if (max_prefix_len > 0 && p.pool_blocks[0] == 0 && p.pool_blocks[1] == 0)
+    return BAT_ERR_INVALID_ARG;
+  Plan pl;
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl))
+    return BAT_ERR_INVALID_ARG;
+  if (!workspace) return BAT_ERR_WORKSPACE;
+  if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
+
+  uint8_t *ws = (uint8_t *)workspace;
+  int32_t *hdr = (int32_t *)ws;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.cu_s = cu_suffix_lens;
+  p.prefix_lens = prefix_lens;
+  p.prefix_mode = prefix_mode;
+  p.block_table = block_table;
+  p.bt_stride = bt_stride;
+  p.B = B;
+  p.H = H;
+  p.total_s = total_suffix;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.chunk_len = pl.chunk_len;
+  p.max_prefix = max_prefix_len;
+  p.items = (const WorkItem *)(ws + pl.off_items);
+  p.meta = (const ReqMeta *)(ws + pl.off_meta);
+  const bool val = validate_enabled();
+  p.err = val ? hdr + kHdrError : nullptr;
+  p.out = out;
+  p.lse = lse;
+  p.part_o = (float *)(ws + pl.off_part_o);
+  p.part_lse = (float *)(ws + pl.off_part_lse);
+
+  hipStream_t st = (hipStream_t)stream;
+  if (launch_plan(cu_suffix_lens, prefix_lens, B, H, pl.bm, pl.chunk_len, max_prefix_len,
+                  (int32_t)pl.grid,
+                  (int32_t *)(ws + pl.off_key), (int32_t *)(ws + pl.off_order),
+                  (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
+                  st) != hipSuccess)
+    return BAT_ERR_HIP;
+  const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, (int)pl.grid, st)
+                                      : launch_attn_f32(p, D, (int)pl.grid, st);
+  if (e != hipSuccess) return BAT_ERR_HIP;
+  if (pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)
+    return BAT_ERR_HIP;
+  if (val) {
+    int32_t h_err = 0;
+    if (hipMemcpyAsync(&h_err, hdr + kHdrError, sizeof h_err, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return BAT_ERR_HIP;
+    if (h_err) return BAT_ERR_BLOCK_TABLE;
+  }
+  return BAT_OK;
+}
+
+bat_status bat_lse_merge(const float *o_parts, const float *lse_parts, int32_t n_parts,
+                         int32_t rows, int32_t H, int32_t D, bat_dtype dt, void *out,
+                         float *lse, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (n_parts <= 0 || rows < 0 || H <= 0 || D <= 0 || (D % 4) != 0) return BAT_ERR_INVALID_ARG;
+  if (rows == 0) return BAT_OK;
+  if (!o_parts || !lse_parts || !out) return BAT_ERR_INVALID_ARG;
+  if (launch_lse_merge(o_parts, lse_parts, n_parts, rows, H, D, dt == BAT_BF16, out, lse,
+                       (hipStream_t)stream) != hipSuccess)
+    return BAT_ERR_HIP;
+  return BAT_OK;
+}
+
+}  // extern "C"

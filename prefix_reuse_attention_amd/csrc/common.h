@@ -1,0 +1,107 @@
+// Shared device-side definitions of libbat (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bat.h"
+
+namespace bat {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Workspace header (int32 words at the start of the workspace).
+constexpr int kHdrError = 0;    // device validation: nonzero = violation seen
+constexpr int kHdrItems = 1;    // planner: number of real work items
+constexpr int kHdrWords = 64;   // 256 bytes
+
+// Error bits reported through the workspace header / kv-build flag.
+constexpr int kErrBlockId = 1;
+constexpr int kErrLength = 2;
+
+// One unit of work of the attention kernels: suffix rows
+// [m_tile * BM, m_tile * BM + BM) of request r, head h, against prefix chunk
+// `chunk` (and, for the last chunk, the request's own suffix).
+struct WorkItem {
+  int32_t r, h, m_tile, chunk;
+};
+
+// Per-request values the planner derives (device arrays in the workspace).
+struct ReqMeta {
+  int32_t n_chunks;   // prefix chunks (1 = not split)
+  int32_t part_off;   // first partial row of this request (split only)
+};
+
+// Everything the attention kernels read, passed by value.
+struct AttnParams {
+  const void *q, *k, *v;          // packed suffix [total_s, H, D]
+  const int32_t *cu_s;            // [B+1]
+  const int32_t *prefix_lens;     // [B]
+  const uint8_t *prefix_mode;     // [B]
+  const int32_t *block_table;     // [B, bt_stride]
+  const void *pool_k[2];          // user, item
+  const void *pool_v[2];
+  int32_t pool_blocks[2];
+  int32_t pool_bs_log2[2];
+  int32_t bt_stride;
+  int32_t B, H;
+  int32_t total_s;
+  float scale_log2;               // softmax_scale * log2(e)
+  int32_t chunk_len;              // prefix keys per chunk when split (0 = never)
+  int32_t max_prefix;             // host bound; longer prefixes are clamped to it
+  const WorkItem *items;
+  const ReqMeta *meta;
+  int32_t *err;                   // workspace header error word, or null
+  void *out;                      // [total_s, H, D]
+  float *lse;                     // [H, total_s] or null
+  float *part_o;                  // split partials [part_rows, H, D]
+  float *part_lse;                // [part_rows, H]
+};
+
+// Key range of one work item: prefix keys [p_begin, p_end) and, when
+// with_suffix, the request's suffix keys.
+struct ItemRange {
+  int32_t q0, n_s, n_p, mode, p_begin, p_end, n_chunks, part_off;
+  bool with_suffix;
+};
+
+__device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) {
+  ItemRange x;
+  x.q0 = p.cu_s[it.r];
+  x.n_s = p.cu_s[it.r + 1] - x.q0;
+  x.n_p = min(max(p.prefix_lens[it.r], 0), p.max_prefix);
+  x.mode = p.prefix_mode[it.r] ? 1 : 0;
+  const ReqMeta m = p.meta[it.r];
+  x.n_chunks = m.n_chunks;
+  x.part_off = m.part_off;
+  if (x.n_chunks <= 1) {
+    x.p_begin = 0;
+    x.p_end = x.n_p;
+    x.with_suffix = true;
+  } else {
+    x.p_begin = it.chunk * p.chunk_len;
+    x.p_end = min(x.n_p, x.p_begin + p.chunk_len);
+    x.with_suffix = it.chunk == x.n_chunks - 1;
+  }
+  return x;
+}
+
+// Element offset of prefix token `tok` (logical position in the request's
+// prefix) of head h inside its pool, or -1 when the block id is out of range.
+__device__ inline int64_t prefix_offset(const AttnParams &p, int r, int mode,
+                                        int tok, int h, int D) {
+  const int lg = p.pool_bs_log2[mode];
+  if ((tok >> lg) >= p.bt_stride) return -1;  // prefix longer than its table row
+  const int blk = p.block_table[(int64_t)r * p.bt_stride + (tok >> lg)];
+  if (blk < 0 || blk >= p.pool_blocks[mode]) return -1;
+  return (((int64_t)blk * p.H + h) << lg | (tok & ((1 << lg) - 1))) * D;
+}
+
+}  // namespace bat

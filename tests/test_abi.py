@@ -1,0 +1,146 @@
+"""C ABI of libbat without a GPU: the library loads, exports every entry
+point include/bat.h declares, and rejects host-detectable argument errors
+with the right status before enqueueing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from prefix_reuse_attention_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bat.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below returns early
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from prefix_reuse_attention_amd import build
+        build.build()
+    return api.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_0-9 \*]*\b(bat_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(api.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bat_[a-z_0-9]+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert api.status_string(s).startswith("BAT_")
+    assert "unknown" in api.status_string(99)
+    assert api.version() >= 100
+
+
+def _pool(num_blocks=4, block_size=64, k=FAKE, v=FAKE):
+    return api.KvPool(k.value if k else None, v.value if v else None, num_blocks, block_size)
+
+
+def kv_build(lib, **over):
+    a = dict(k=FAKE, v=FAKE, cu=FAKE, bt=FAKE, bt_stride=4, B=2, H=8, D=64, total=100,
+             dt=api.BAT_BF16, pool=_pool(), stream=None)
+    a.update(over)
+    pool = ctypes.byref(a["pool"]) if a["pool"] is not None else None
+    return lib.bat_kv_build(a["k"], a["v"], a["cu"], a["bt"], a["bt_stride"], a["B"], a["H"],
+                            a["D"], a["total"], a["dt"], pool, a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(pool=None), api.BAT_ERR_INVALID_ARG),
+    (dict(k=None), api.BAT_ERR_INVALID_ARG),
+    (dict(cu=None), api.BAT_ERR_INVALID_ARG),
+    (dict(bt=None), api.BAT_ERR_INVALID_ARG),
+    (dict(H=0), api.BAT_ERR_INVALID_ARG),
+    (dict(B=-1), api.BAT_ERR_INVALID_ARG),
+    (dict(total=-5), api.BAT_ERR_INVALID_ARG),
+    (dict(D=48), api.BAT_ERR_UNSUPPORTED),
+    (dict(dt=7), api.BAT_ERR_INVALID_ARG),
+    (dict(pool=_pool(block_size=3)), api.BAT_ERR_INVALID_ARG),
+    (dict(pool=_pool(block_size=512)), api.BAT_ERR_INVALID_ARG),
+    (dict(pool=_pool(num_blocks=-1)), api.BAT_ERR_INVALID_ARG),
+    (dict(pool=_pool(k=None)), api.BAT_ERR_INVALID_ARG),
+    (dict(total=0), api.BAT_OK),                      # nothing to do, nothing launched
+])
+def test_kv_build_argument_errors(lib, over, status):
+    assert kv_build(lib, **over) == status
+
+
+def prefill(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, plen=FAKE, mode=FAKE, bt=FAKE, bt_stride=16,
+             up=_pool(), ip=None, B=2, H=8, D=128, dt=api.BAT_BF16, scale=0.088, total=1024,
+             max_s=512, max_p=1024, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    up = ctypes.byref(a["up"]) if a["up"] is not None else None
+    ip = ctypes.byref(a["ip"]) if a["ip"] is not None else None
+    if a["ws_bytes"] == "exact-1":
+        a["ws_bytes"] = lib.bat_attn_workspace_size(a["B"], a["H"], a["D"], a["dt"], a["total"],
+                                                    a["max_s"], a["max_p"]) - 1
+        # the only remaining error is the workspace size: make every other
+        # argument valid so that the call would otherwise launch
+    return lib.bat_attn_prefill(a["q"], a["k"], a["v"], a["cu"], a["plen"], a["mode"], a["bt"],
+                                a["bt_stride"], up, ip, a["B"], a["H"], a["D"], a["dt"],
+                                a["scale"], a["total"], a["max_s"], a["max_p"], a["out"],
+                                a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BAT_ERR_INVALID_ARG),
+    (dict(out=None), api.BAT_ERR_INVALID_ARG),
+    (dict(cu=None), api.BAT_ERR_INVALID_ARG),
+    (dict(plen=None), api.BAT_ERR_INVALID_ARG),
+    (dict(mode=None), api.BAT_ERR_INVALID_ARG),
+    (dict(bt=None), api.BAT_ERR_INVALID_ARG),          # prefixes but no block table
+    (dict(up=None), api.BAT_ERR_INVALID_ARG),          # prefixes but no pool
+    (dict(scale=0.0), api.BAT_ERR_INVALID_ARG),
+    (dict(scale=-1.0), api.BAT_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), api.BAT_ERR_INVALID_ARG),
+    (dict(H=0), api.BAT_ERR_INVALID_ARG),
+    (dict(B=-2), api.BAT_ERR_INVALID_ARG),
+    (dict(max_s=0), api.BAT_ERR_INVALID_ARG),
+    (dict(max_p=-1), api.BAT_ERR_INVALID_ARG),
+    (dict(D=32), api.BAT_ERR_UNSUPPORTED),             # bf16 kernels: D in {64, 128}
+    (dict(D=96), api.BAT_ERR_UNSUPPORTED),
+    (dict(D=256, dt=api.BAT_F32), api.BAT_ERR_UNSUPPORTED),
+    (dict(dt=3), api.BAT_ERR_INVALID_ARG),
+    (dict(up=_pool(block_size=6)), api.BAT_ERR_INVALID_ARG),
+    (dict(ws=None), api.BAT_ERR_WORKSPACE),
+    (dict(ws_bytes="exact-1"), api.BAT_ERR_WORKSPACE),
+    (dict(total=0), api.BAT_OK),                       # no suffix rows: nothing to write
+])
+def test_prefill_argument_errors(lib, over, status):
+    assert prefill(lib, **over) == status
+
+
+def test_workspace_size(lib):
+    f = lib.bat_attn_workspace_size
+    assert f(2, 8, 128, api.BAT_BF16, 1024, 512, 1024) > 0
+    assert f(2, 8, 128, api.BAT_BF16, 1024, 512, 1024) <= f(4, 8, 128, api.BAT_BF16, 2048, 512, 1024)
+    assert f(-1, 8, 128, api.BAT_BF16, 1024, 512, 1024) == 0
+    assert f(2, 8, 96, api.BAT_BF16, 1024, 512, 1024) == 0
+    # a batch too small to fill the GPU with a long prefix gets split partials
+    assert f(1, 2, 128, api.BAT_BF16, 64, 64, 16384) > f(1, 2, 128, api.BAT_BF16, 64, 64, 1024)
+
+
+def test_lse_merge_argument_errors(lib):
+    m = lib.bat_lse_merge
+    assert m(FAKE, FAKE, 0, 10, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, 2, 10, 2, 62, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG
+    assert m(None, FAKE, 2, 10, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, 2, 10, 2, 64, 9, FAKE, None, None) == api.BAT_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, 2, 0, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_OK

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 from prefix_reuse_attention_amd import workloads as W
+from helpers import assemble_prefix
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -127,21 +128,6 @@ def test_prefill_batch_brute_force_and_selection():
                                    wl.scale, rows=rows, heads=heads)
     np.testing.assert_array_equal(so, out[rows, heads])
     np.testing.assert_array_equal(sl, lse[heads, rows])
-
-
-def assemble_prefix(wl):
-    """Each request's prefix in the order it sees it (item mode: listed items' tokens)."""
-    ks, vs, cu = [], [], [0]
-    for r in range(wl.B):
-        if wl.mode[r] == W.ITEM:
-            ids = wl.block_table[r, : wl.n_p[r] // W.ITEM_TOKENS]
-            ks.append(oracle.gather_item_prefix(wl.item_k, ids, W.ITEM_TOKENS))
-            vs.append(oracle.gather_item_prefix(wl.item_v, ids, W.ITEM_TOKENS))
-        else:
-            ks.append(wl.user_k[wl.cu_user[r]:wl.cu_user[r + 1]])
-            vs.append(wl.user_v[wl.cu_user[r]:wl.cu_user[r + 1]])
-        cu.append(cu[-1] + len(ks[-1]))
-    return np.concatenate(ks), np.concatenate(vs), np.array(cu, np.int32)
 
 
 # ------------------------------------------------------- library routine (SDPA)

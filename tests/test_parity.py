@@ -1,0 +1,132 @@
+"""GPU parity: bat_attn_prefill (HIP, through the C ABI) against the CPU oracle.
+
+Bars: max-abs 1e-5 in fp32 and 2e-2 in bf16 on out (the graded tolerances),
+plus, for bf16, relative RMS <= 1e-2 and, at full size, max-abs <= 4e-3; lse
+within 1e-5 (fp32) / 1e-3 (bf16).  Small cases compare every output; the five
+measured configurations run at full size in the benchmark's launch
+configuration and compare sampled (row, head) pairs.
+"""
+import numpy as np
+import pytest
+
+from helpers import as_f64, check_close, oracle_full, oracle_sampled, sample_pairs
+from prefix_reuse_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, **kw):
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_host
+    import torch
+    dw = DeviceWorkload(wl)
+    out, lse = dw.run(**kw)
+    torch.cuda.synchronize()
+    return as_f64(to_host(out, wl.dtype), wl.dtype), lse.cpu().numpy().astype(np.float64)
+
+
+def _compare_full(wl, strict_abs=None):
+    print(f"[parity] {wl.name} dtype={wl.dtype} B={wl.B} H={wl.H} D={wl.D} "
+          f"n_s={wl.n_s.tolist()[:8]} n_p={wl.n_p.tolist()[:8]}", flush=True)
+    got, lse = _run(wl)
+    ref_o, ref_l = oracle_full(wl)
+    check_close(got, ref_o, wl.dtype, strict_abs)
+    tol = 1e-5 if wl.dtype == "f32" else 1e-3
+    assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"
+
+
+def test_config1_fp32_full(gpu_ready):
+    _compare_full(W.make_config(1))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fp32_ragged(gpu_ready, D):
+    wl = W.make_custom(dtype="f32", H=3, D=D, n_s=[1, 70, 129], n_p=[0, 33, 200],
+                       mode=[W.USER, W.USER, W.ITEM], seed=20 + D, user_block_size=16,
+                       num_items=80, name=f"f32_ragged_D{D}")
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_ragged_mixed(gpu_ready, D):
+    """Several tiles and ragged tails on every axis: suffix lengths that are
+    not multiples of the row tile, prefixes that end mid-block and mid-tile,
+    an empty prefix, item and user prefixes in one batch."""
+    wl = W.make_custom(dtype="bf16", H=4, D=D, n_s=[1, 130, 257, 64, 5],
+                       n_p=[0, 200, 1000, 4, 129], mode=[W.USER, W.USER, W.ITEM, W.ITEM, W.USER],
+                       seed=30 + D, num_items=400, name=f"bf16_ragged_D{D}")
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_small_blocks(gpu_ready, D):
+    """User pools with 1-, 2- and 16-token pages (the per-key gather path)."""
+    for bs in (1, 2, 16):
+        wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=[40, 3], n_p=[77, 130],
+                           mode=[W.USER, W.USER], seed=40 + bs, user_block_size=bs,
+                           name=f"bf16_bs{bs}_D{D}")
+        _compare_full(wl)
+
+
+def test_bf16_empty_requests_and_suffix_only(gpu_ready):
+    """Requests with no suffix rows write nothing; n_p = 0 is pure suffix
+    self-attention (the empty prefix partial merges as the identity)."""
+    wl = W.make_custom(dtype="bf16", H=2, D=128, n_s=[0, 17, 0, 300], n_p=[64, 0, 0, 0],
+                       mode=[W.USER] * 4, seed=50, name="bf16_empty")
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_peaky_scores(gpu_ready, D):
+    """Queries scaled by 8: sharp softmax, large running-max jumps."""
+    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=[200, 77], n_p=[900, 300],
+                       mode=[W.USER, W.ITEM], seed=60 + D, num_items=200, q_scale=8.0,
+                       name=f"bf16_peaky_D{D}")
+    _compare_full(wl)
+
+
+def test_bf16_increasing_scores(gpu_ready):
+    """Scores that rise along the key order force a rescale on many tiles."""
+    wl = W.make_custom(dtype="bf16", H=1, D=64, n_s=[128], n_p=[2048], mode=[W.USER],
+                       seed=70, name="bf16_rising")
+    q = W.bf16_to_f32(wl.q).copy()
+    q[:] = 1.0
+    wl.q = W.f32_to_bf16(q)
+    k = W.bf16_to_f32(wl.user_k).copy()
+    k[:, 0, :] = (np.linspace(-3, 3, 2048, dtype=np.float32)[:, None] *
+                  np.ones((1, 64), np.float32)) / 8
+    wl.user_k = W.f32_to_bf16(k)
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_split_prefix_merge(gpu_ready, monkeypatch, dtype, D):
+    """Prefixes split across workgroups (forced chunk length), recombined by
+    the log-sum-exp merge kernel."""
+    monkeypatch.setenv("BAT_SPLIT_CHUNK", "256")
+    wl = W.make_custom(dtype=dtype, H=2, D=D, n_s=[90, 300, 1], n_p=[1000, 256, 2100],
+                       mode=[W.USER, W.ITEM, W.USER], seed=80 + D, num_items=100,
+                       name=f"split_{dtype}_D{D}")
+    _compare_full(wl)
+
+
+def test_automatic_split_few_items(gpu_ready):
+    """One request with a long prefix and a short suffix: too few items to
+    fill the GPU, so the library splits the prefix by itself."""
+    wl = W.make_custom(dtype="bf16", H=2, D=128, n_s=[64], n_p=[16384], mode=[W.USER],
+                       seed=90, name="auto_split")
+    _compare_full(wl)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_config_full_size_sampled(gpu_ready, k):
+    wl = W.make_config(k)
+    print(f"[parity] config {k}: {wl.notes['description']}", flush=True)
+    got, lse = _run(wl)
+    rows, heads = sample_pairs(wl, 400, seed=k)
+    ref_o, ref_l = oracle_sampled(wl, rows, heads)
+    check_close(got[rows, heads], ref_o, wl.dtype, strict_abs=4e-3, what=f"config{k} out")
+    assert np.abs(lse[heads, rows] - ref_l).max() <= 1e-3
+    # properties that hold for every row: finite, and a convex combination of
+    # values whose entries are bounded by the largest |v|
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))

@@ -53,6 +53,9 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (scales the "
+                         "HBM byte counters of rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -62,6 +65,15 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}), flush=True)
+        return
     from prefix_reuse_attention_amd import api
     from prefix_reuse_attention_amd import workloads as W
     from prefix_reuse_attention_amd.device import DeviceWorkload
@@ -81,12 +93,15 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     dw.upload_prefix()
     dw.alloc_pools()
+    dw.build_kv()          # first launch also loads the code object: untimed
     torch.cuda.synchronize()
+    reps = 5
     ev0.record(stream)
-    dw.build_kv()
+    for _ in range(reps):  # rebuilding the same pool is idempotent
+        dw.build_kv()
     ev1.record(stream)
     torch.cuda.synchronize()
-    build_ms = ev0.elapsed_time(ev1)
+    build_ms = ev0.elapsed_time(ev1) / reps
     build_bytes = dw.prefix_bytes()
     dw.drop_prefix_source()
     ws = dw.workspace()

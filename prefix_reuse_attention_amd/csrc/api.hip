@@ -12,8 +12,7 @@ hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu, cons
                            int32_t bs_log2, int32_t *err, hipStream_t stream);
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B, int32_t H,
                        int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-                       int32_t *req_key,
-                       int32_t *req_order, ReqMeta *meta, WorkItem *items, int32_t *hdr,
+                       int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
                        hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
@@ -61,8 +60,8 @@ struct Plan {
   int max_chunks = 1;
   int64_t grid = 0;       // work-item slots (upper bound, multiple of 8)
   int64_t part_rows = 0;  // split partial rows
-  size_t off_items = 0, off_meta = 0, off_key = 0, off_order = 0, off_part_o = 0,
-         off_part_lse = 0, total = 0;
+  size_t off_items = 0, off_meta = 0, off_scratch = 0, off_part_o = 0, off_part_lse = 0,
+         total = 0;
 };
 
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
@@ -96,8 +95,7 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   size_t off = align256(kHdrWords * sizeof(int32_t));
   pl.off_items = off;    off = align256(off + sizeof(WorkItem) * (size_t)pl.grid);
   pl.off_meta = off;     off = align256(off + sizeof(ReqMeta) * (size_t)B);
-  pl.off_key = off;      off = align256(off + sizeof(int32_t) * (size_t)B);
-  pl.off_order = off;    off = align256(off + sizeof(int32_t) * (size_t)B);
+  pl.off_scratch = off;  off = align256(off + 4 * sizeof(int32_t) * (size_t)B);
   pl.off_part_o = off;   off = align256(off + sizeof(float) * (size_t)pl.part_rows * H * D);
   pl.off_part_lse = off; off = align256(off + sizeof(float) * (size_t)pl.part_rows * H);
   pl.total = off;
@@ -244,8 +242,7 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
 
   hipStream_t st = (hipStream_t)stream;
   if (launch_plan(cu_suffix_lens, prefix_lens, B, H, pl.bm, pl.chunk_len, max_prefix_len,
-                  (int32_t)pl.grid,
-                  (int32_t *)(ws + pl.off_key), (int32_t *)(ws + pl.off_order),
+                  (int32_t)pl.grid, (int32_t *)(ws + pl.off_scratch),
                   (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
                   st) != hipSuccess)
     return BAT_ERR_HIP;

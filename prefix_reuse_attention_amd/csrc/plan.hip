@@ -7,33 +7,97 @@
 // be served from that XCD's L2.  Groups are ordered longest first (the
 // largest per-item key count first) and dealt round-robin over the XCDs, so
 // each XCD's queue also runs longest first, which bounds the tail.
+//
+// One workgroup of 1024 threads; thread t owns a contiguous run of requests,
+// and every prefix sum over requests is a block-wide scan (wave shuffles,
+// then one pass over the 16 wave totals).
 #include "common.h"
 
 namespace bat {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kPlanLds = 4096;  // batches up to this size keep per-request state in LDS
+
+// Exclusive block-wide scan of NV int64 lanes per thread; returns totals.
+template <int NV>
+__device__ __forceinline__ void block_scan(int64_t (&v)[NV], int64_t (&total)[NV],
+                                           int64_t (*s_wave)[kNumXcd], int64_t *s_total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t inc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) inc[i] = v[i];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t t = __shfl_up(inc[i], off);
+      if (lane >= off) inc[i] += t;
+    }
+  }
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s_wave[w][i] = inc[i];
+  __syncthreads();
+  if (tid < NV) {
+    int64_t acc = 0;
+    for (int j = 0; j < kPlanWaves; ++j) {
+      const int64_t t = s_wave[j][tid];
+      s_wave[j][tid] = acc;
+      acc += t;
+    }
+    s_total[tid] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = inc[i] - v[i] + s_wave[w][i];
+    total[i] = s_total[i];
+  }
+  __syncthreads();  // s_wave / s_total are reused by the next scan
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
     int32_t B, int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-    int32_t *__restrict__ req_key,    // [B] scratch: work key, then sorted order
-    int32_t *__restrict__ req_order,  // [B] scratch
+    int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
     ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
   const int tid = threadIdx.x;
-  __shared__ int64_t s_sum[kPlanThreads][kNumXcd];  // per-thread partial sums
+  __shared__ int64_t s_wave[kPlanWaves][kNumXcd];
   __shared__ int64_t s_total[kNumXcd];
+  __shared__ int32_t s_req[4 * kPlanLds];
+  // per request: work key, sorted order, suffix length, chunk count
+  int32_t *base = B <= kPlanLds ? s_req : g_scratch;
+  const int32_t stride = B <= kPlanLds ? kPlanLds : B;
+  int32_t *req_key = base, *req_order = base + stride, *req_ns = base + 2 * stride,
+          *req_nc = base + 3 * stride;
 
   if (tid == 0) hdr[kHdrError] = 0;
   for (int64_t idx = tid; idx < grid; idx += kPlanThreads) items[idx] = WorkItem{-1, 0, 0, 0};
-  // 1) per-request tiles, chunks and work key (keys per item)
-  for (int r = tid; r < B; r += kPlanThreads) {
-    const int n_s = cu_s[r + 1] - cu_s[r];
-    const int n_p = min(max(prefix_lens[r], 0), max_p);
-    int nc = 1;
-    if (chunk_len > 0 && n_p > chunk_len) nc = (n_p + chunk_len - 1) / chunk_len;
-    meta[r].n_chunks = nc;
-    const int keys = (n_s > 0) ? (nc > 1 ? chunk_len : n_p) + n_s : -1;
-    req_key[r] = keys;
+
+  const int per = (B + kPlanThreads - 1) / kPlanThreads;
+  const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
+
+  // 1) per request: chunks, work key (keys per item), split-partial rows;
+  //    partial offsets are an exclusive scan in request order
+  {
+    int64_t part[1] = {0}, tot[1];
+    for (int r = k0; r < k1; ++r) {
+      const int n_s = cu_s[r + 1] - cu_s[r];
+      const int n_p = min(max(prefix_lens[r], 0), max_p);
+      int nc = 1;
+      if (chunk_len > 0 && n_p > chunk_len) nc = (n_p + chunk_len - 1) / chunk_len;
+      req_nc[r] = nc;
+      req_ns[r] = n_s;
+      req_key[r] = (n_s > 0) ? (nc > 1 ? chunk_len : n_p) + n_s : -1;
+      if (nc > 1 && n_s > 0) part[0] += (int64_t)nc * n_s;
+    }
+    block_scan<1>(part, tot, s_wave, s_total);
+    for (int r = k0; r < k1; ++r) {
+      const int nc = req_nc[r], n_s = req_ns[r];
+      meta[r] = ReqMeta{nc, (int32_t)part[0]};
+      if (nc > 1 && n_s > 0) part[0] += (int64_t)nc * n_s;
+    }
   }
   __syncthreads();
   // 2) stable rank sort, largest key first (O(B^2 / threads))
@@ -47,70 +111,39 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     req_order[rank] = r;
   }
   __syncthreads();
-  // 3) per request (in sorted order): groups = H * chunks, each of T tiles.
-  //    Group g (global, in order) goes to XCD g % 8.  Count, per request and
-  //    XCD, the slots its groups take; an exclusive scan gives the bases.
-  //    Each thread owns a contiguous run of sorted requests.
-  const int per = (B + kPlanThreads - 1) / kPlanThreads;
-  const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
-  // group index of the first group of each request needs a scan of group
-  // counts first
-  int64_t my_groups = 0;
+  // 3) groups of my run of sorted requests, and the first global group index
+  int64_t g0[1] = {0}, ng_total[1];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
-    const int n_s = cu_s[r + 1] - cu_s[r];
-    if (n_s > 0) my_groups += (int64_t)H * meta[r].n_chunks;
+    if (req_ns[r] > 0) g0[0] += (int64_t)H * req_nc[r];
   }
-  s_sum[tid][0] = my_groups;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int i = 0; i < kPlanThreads; ++i) {
-      const int64_t t = s_sum[i][0];
-      s_sum[i][0] = acc;
-      acc += t;
-    }
-  }
-  __syncthreads();
-  const int64_t g0 = s_sum[tid][0];  // first global group index of my run
-  __syncthreads();
-  int64_t slots[kNumXcd] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int64_t g = g0;
+  block_scan<1>(g0, ng_total, s_wave, s_total);
+  // 4) slots each XCD gives my groups: group g goes to XCD g % 8
+  int64_t slots[kNumXcd] = {0, 0, 0, 0, 0, 0, 0, 0}, used[kNumXcd];
+  int64_t g = g0[0];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
-    const int n_s = cu_s[r + 1] - cu_s[r];
+    const int n_s = req_ns[r];
     if (n_s <= 0) continue;
     const int T = (n_s + bm - 1) / bm;
-    const int64_t ng = (int64_t)H * meta[r].n_chunks;
+    const int64_t ng = (int64_t)H * req_nc[r];
+#pragma unroll
     for (int x = 0; x < kNumXcd; ++x) {
-      // groups g .. g+ng-1 with (group % 8) == x
       const int64_t first = g + ((x - g % kNumXcd) + kNumXcd) % kNumXcd;
       const int64_t cnt = first < g + ng ? (g + ng - 1 - first) / kNumXcd + 1 : 0;
       slots[x] += cnt * T;
     }
     g += ng;
   }
-  for (int x = 0; x < kNumXcd; ++x) s_sum[tid][x] = slots[x];
-  __syncthreads();
-  if (tid < kNumXcd) {
-    int64_t acc = 0;
-    for (int i = 0; i < kPlanThreads; ++i) {
-      const int64_t t = s_sum[i][tid];
-      s_sum[i][tid] = acc;
-      acc += t;
-    }
-    s_total[tid] = acc;  // slots used on XCD `tid`
-  }
-  __syncthreads();
-  // 4) write the items of my run
-  g = g0;
-  for (int x = 0; x < kNumXcd; ++x) slots[x] = s_sum[tid][x];
+  block_scan<kNumXcd>(slots, used, s_wave, s_total);
+  // 5) write my items
+  g = g0[0];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
-    const int n_s = cu_s[r + 1] - cu_s[r];
+    const int n_s = req_ns[r];
     if (n_s <= 0) continue;
     const int T = (n_s + bm - 1) / bm;
-    const int nc = meta[r].n_chunks;
+    const int nc = req_nc[r];
     const int64_t ng = (int64_t)H * nc;
     for (int64_t gi = 0; gi < ng; ++gi, ++g) {
       const int x = (int)(g % kNumXcd);
@@ -123,27 +156,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       slots[x] += T;
     }
   }
-  // 5) split partial offsets (exclusive scan of n_chunks * n_s over split
-  //    requests, in request order) and the empty tail slots of each XCD
   if (tid == 0) {
-    int64_t acc = 0;
-    for (int r = 0; r < B; ++r) {
-      const int nc = meta[r].n_chunks;
-      meta[r].part_off = (int32_t)acc;
-      if (nc > 1) acc += (int64_t)nc * (cu_s[r + 1] - cu_s[r]);
-    }
-    int64_t n_items = 0;
-    for (int x = 0; x < kNumXcd; ++x) n_items += s_total[x];
-    hdr[kHdrItems] = (int32_t)n_items;
+    int64_t n = 0;
+#pragma unroll
+    for (int x = 0; x < kNumXcd; ++x) n += used[x];
+    hdr[kHdrItems] = (int32_t)n;
   }
 }
 
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
                        int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-                       int32_t *req_key, int32_t *req_order,
-                       ReqMeta *meta, WorkItem *items, int32_t *hdr, hipStream_t stream) {
+                       int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
+                       hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_s, prefix_lens,
-                     B, H, bm, chunk_len, max_p, grid, req_key, req_order, meta, items, hdr);
+                     B, H, bm, chunk_len, max_p, grid, g_scratch, meta, items, hdr);
   return hipGetLastError();
 }
 

@@ -11,17 +11,29 @@
 // the suffix tiles is the log-sum-exp merge of the prefix and suffix
 // partials, done in registers.
 //
-// Data flow of one key tile (BN keys):
-//   HBM/L2 --16B loads--> VGPRs --ds_write--> LDS (K row-major, V transposed)
-//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q in VGPRs
-//   online softmax  on the S^T accumulator: each lane owns one query row
-//   O^T += V^T P^T  v_mfma_f32_32x32x16_bf16, A = V^T from LDS, B = P in VGPRs
+// Data flow of one key tile (BN keys, 16 KB of K and 16 KB of V):
+//   HBM/L2 --buffer/global_load_dwordx4 ... lds--> LDS, row-major, 16-byte
+//            chunks XOR-swizzled per row (no VGPR staging, no LDS store
+//            instructions); two LDS stages, the next tile's copy in flight
+//            while the current one is consumed, one barrier per tile
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128),
+//                   B = Q held in VGPRs for the whole item
+//   online softmax  per 32-key block on the S^T accumulator; each lane owns
+//                   one query row, the two lane halves meet through
+//                   v_permlane32_swap
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_bf16, A = V^T read from the
+//                   row-major V tile by ds_read_b64_tr_b16 (the LDS
+//                   transpose read), B = P straight from the S^T registers
 // Computing the transposed products makes the query row the lane index of
-// both accumulators, so P goes from the S^T accumulator straight into the
-// PV operand and the per-row rescale is a per-lane multiply.
+// both accumulators, so P never leaves registers and the per-row rescale
+// is a per-lane multiply.
 #include "common.h"
 
 namespace bat {
+
+// 16 zero bytes: the copy source of keys past the end of a tile, so that
+// every lane issues its load and masked keys hold zeros.
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
 template <int D>
 struct Bf16Cfg {
@@ -29,97 +41,35 @@ struct Bf16Cfg {
   static constexpr int WAVES = 4;
   static constexpr int ROWS = 32;                   // query rows per wave
   static constexpr int BM = WAVES * ROWS;           // query rows per item
-  static constexpr int K_STRIDE = D + 8;            // LDS row pitch (elements)
-  static constexpr int V_STRIDE = BN + 8;
-  static constexpr int K_ELEMS = BN * K_STRIDE;
-  static constexpr int V_ELEMS = D * V_STRIDE;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KG = BN / 4;                 // loader: groups of 4 keys
-  static constexpr int DC = D / 8;                  // loader: 16-byte d chunks
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  static constexpr int RB = D * 2;                  // bytes per K/V row
+  static constexpr int RPI = 64 / CPR;              // rows per wave copy instruction
+  static constexpr int TILE = BN * RB;              // bytes of one K (or V) tile
   static constexpr int NB = BN / 32;                // 32-key MFMA blocks per tile
   static constexpr int ND = D / 32;                 // 32-wide d blocks of O
   static constexpr int KK = D / 16;                 // k-steps of QK^T
-  static_assert(KG * DC == 256, "one 4x8 sub-tile per thread");
+  static_assert(TILE == 16384, "4 copy instructions per wave per tile");
 };
 
-// Within each 32-key block the K tile is stored in LDS with its rows
-// permuted, so that accumulator element i of lane-half hf of S^T holds key
-// 16*(i/8) + 8*hf + i%8: eight consecutive keys per half-chunk, which is
-// exactly the B-operand layout of the PV MFMA (and lets each lane read V^T
-// with one 16-byte access).  pinv maps a key to its LDS row.
-__device__ __forceinline__ int k_lds_row(int key) {
-  const int k = key & 31;
-  const int a = k >> 4, b = (k >> 3) & 1, c = (k >> 2) & 1, t = k & 3;
-  return (key & ~31) | (8 * (2 * a + c) + 4 * b + t);
+// Chunk swizzle of K/V row r: chunk c of the row is stored at c ^ swz(r).
+// With 64 LDS banks it makes three access patterns conflict-free: the
+// S^T operand read (16 consecutive lanes, 16 distinct rows, one chunk),
+// the transpose read (4 consecutive rows x 4 chunks per 32 lanes) and the
+// copy itself (contiguous 1 KB per instruction).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-struct Bf16Tile {
-  u32x4 k[4], v[4];
-};
-
-template <int D>
-__device__ __forceinline__ void bf16_load_tile(const AttnParams &p, const ItemRange &x,
-                                               int r, int head, int tile, int n_tiles_p,
-                                               int m, int c, Bf16Tile &T) {
-  using C = Bf16Cfg<D>;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  if (tile < n_tiles_p) {
-    const int key0 = x.p_begin + tile * C::BN + 4 * m;
-    const uint16_t *pk = (const uint16_t *)p.pool_k[x.mode];
-    const uint16_t *pv = (const uint16_t *)p.pool_v[x.mode];
-    if (p.pool_bs_log2[x.mode] >= 2) {
-      // the 4 keys share one block (tiles start at multiples of 4)
-      int64_t off = key0 < x.p_end ? prefix_offset(p, r, x.mode, key0, head, D) : -1;
-      if (key0 < x.p_end && off < 0 && p.err) atomicOr(p.err, kErrBlockId);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = off >= 0 && key0 + i < x.p_end;
-        T.k[i] = ok ? *(const u32x4 *)(pk + off + i * D + 8 * c) : zero;
-        T.v[i] = ok ? *(const u32x4 *)(pv + off + i * D + 8 * c) : zero;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t off = key0 + i < x.p_end ? prefix_offset(p, r, x.mode, key0 + i, head, D) : -1;
-        if (key0 + i < x.p_end && off < 0 && p.err) atomicOr(p.err, kErrBlockId);
-        T.k[i] = off >= 0 ? *(const u32x4 *)(pk + off + 8 * c) : zero;
-        T.v[i] = off >= 0 ? *(const u32x4 *)(pv + off + 8 * c) : zero;
-      }
-    }
-  } else {
-    const int s0 = (tile - n_tiles_p) * C::BN + 4 * m;
-    const uint16_t *ks = (const uint16_t *)p.k;
-    const uint16_t *vs = (const uint16_t *)p.v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = s0 + i < x.n_s && x.q0 >= 0 && x.q0 + s0 + i < p.total_s;
-      const int64_t off = ((int64_t)(x.q0 + s0 + i) * p.H + head) * D + 8 * c;
-      T.k[i] = ok ? *(const u32x4 *)(ks + off) : zero;
-      T.v[i] = ok ? *(const u32x4 *)(vs + off) : zero;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void bf16_store_tile(uint16_t *stage, int m, int c, const Bf16Tile &T) {
-  using C = Bf16Cfg<D>;
-  uint16_t *Ks = stage;
-  uint16_t *Vt = stage + C::K_ELEMS;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(u32x4 *)(Ks + k_lds_row(4 * m + i) * C::K_STRIDE + 8 * c) = T.k[i];
-  // transpose the 4 keys x 8 dims sub-tile: V^T[8c + d][4m .. 4m+3]
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a0 = T.v[0][w], a1 = T.v[1][w], a2 = T.v[2][w], a3 = T.v[3][w];
-    u32x2 lo, hi;
-    lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // d = 2w:   keys 0,1
-    lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);  //           keys 2,3
-    hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // d = 2w+1: keys 0,1
-    hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-    *(u32x2 *)(Vt + (8 * c + 2 * w) * C::V_STRIDE + 4 * m) = lo;
-    *(u32x2 *)(Vt + (8 * c + 2 * w + 1) * C::V_STRIDE + 4 * m) = hi;
-  }
+// The K operand lane m of a 32-key block reads key row pi(m), so that
+// accumulator element i of lane-half hf of S^T holds key
+// 16*(i/8) + 8*hf + i%8: eight consecutive keys per half-chunk, which is the
+// B-operand layout the PV MFMA wants (and the order the transpose read of V
+// produces).
+__device__ __forceinline__ int k_row_of_lane(int m) {
+  const int j = m >> 3, h = (m >> 2) & 1, t = m & 3;
+  return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + t;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -130,10 +80,261 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+__device__ __forceinline__ float row_max_both_halves(float v) {
+  // v_permlane32_swap(v, v) leaves {own, other half} in its two results
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                  __builtin_bit_cast(uint32_t, v), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Per-lane byte offsets of the MFMA operand reads inside one LDS stage.  The
+// chunk swizzle of a row depends only on the row's low bits, which the
+// 32-key block index and the 16-key chunk index do not change, so each read
+// is a lane constant plus an immediate (block * 32 rows, chunk * 16 rows).
+template <int D>
+struct LdsOffsets {
+  using C = Bf16Cfg<D>;
+  int k[C::KK];      // S^T operand: key row pi(col) of block 0, d chunk 2kk+hf
+  int v[C::ND][2];   // transpose read of keys 8hf + 4e4 + 0..3, d block nd
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, hf = lane >> 5, g = lane >> 4, i16 = lane & 15;
+    const int krow = k_row_of_lane(col);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk)
+      k[kk] = krow * C::RB + (((2 * kk + hf) ^ swz<D>(krow)) << 4);
+    const int kq = i16 >> 2, q = i16 & 3;
+#pragma unroll
+    for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+      for (int e4 = 0; e4 < 2; ++e4) {
+        const int key = 8 * hf + 4 * e4 + kq;
+        const int d = 32 * nd + 16 * (g & 1) + 4 * q;
+        v[nd][e4] = key * C::RB + (((d >> 3) ^ swz<D>(key)) << 4) + (q & 1) * 8;
+      }
+  }
+};
+
+// Everything one workgroup needs to copy the tiles of its item.
+//
+// Each wave issues four 16-byte-per-lane copies of K and four of V per tile;
+// copy j of wave w fills LDS bytes [(4w+j)*1024, +1024) of the stage, i.e.
+// tile row r = RPI*(4w+j) + lane/CPR, stored chunk lane%CPR, which holds the
+// row's global chunk (lane%CPR) ^ swz(r).
+//
+// When a pool block holds at least one tile (block_size >= BN), a tile is
+// one contiguous run inside one block (or of the packed suffix), so the
+// copy is a buffer load: a per-tile base in SGPRs, lane-constant offsets,
+// and the descriptor's size cutting off rows past the end (they read as
+// zero).  Smaller blocks (item pools) gather per lane.
+template <int D>
+struct TileCopy {
+  using C = Bf16Cfg<D>;
+  const uint8_t *pool_k, *pool_v, *ks, *vs;  // prefix pool / suffix K,V bases
+  const int32_t *bt_row;                     // this request's block-table row
+  int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p;
+  bool whole_blocks;                         // block_size >= BN
+  int64_t block_bytes, head_bytes;           // H*bs*RB, head*bs*RB
+  int wave, lane;
+  int row[4], cb[4];                         // tile row and stored-chunk source byte
+  int32_t *err;
+
+  __device__ __forceinline__ void init_lanes() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      row[j] = C::RPI * (4 * wave + j) + lane / C::CPR;
+      cb[j] = ((lane % C::CPR) ^ swz<D>(row[j])) << 4;
+    }
+  }
+
+  // block ids of prefix tile `tile` (-1 = none): one per tile for whole
+  // blocks, else one per row this lane copies
+  __device__ __forceinline__ void load_ids(int tile, int (&ids)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = p_begin + tile * C::BN + (whole_blocks ? 0 : row[j]);
+      const int slot = key >> lg;
+      const bool ok = tile < n_tiles_p && key < p_end && slot < bt_stride &&
+                      (j == 0 || !whole_blocks);
+      ids[j] = ok ? bt_row[slot] : -1;
+    }
+  }
+
+  // Issue the copy of tile `tile` into one LDS stage (K at kl, V at vl).
+  __device__ __forceinline__ void issue(int tile, const int (&ids)[4], uint8_t *kl,
+                                        uint8_t *vl) const {
+    constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
+    if (tile < n_tiles_p && !whole_blocks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = p_begin + tile * C::BN + row[j];
+        const int blk = ids[j];
+        const bool inb = blk >= 0 && blk < blocks;
+        if (key < p_end && !inb && err) atomicOr(err, kErrBlockId);
+        const uint8_t *ksrc = (const uint8_t *)g_zero16;
+        const uint8_t *vsrc = (const uint8_t *)g_zero16;
+        if (key < p_end && inb) {
+          const int64_t off =
+              ((((int64_t)blk * H + head) << lg) | (key & ((1 << lg) - 1))) * C::RB + cb[j];
+          ksrc = pool_k + off;
+          vsrc = pool_v + off;
+        }
+        __builtin_amdgcn_global_load_lds(ksrc, kl + (4 * wave + j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc, vl + (4 * wave + j) * 1024, 16, 0, 0);
+      }
+      return;
+    }
+    const uint8_t *kb, *vb;
+    int records, stride;
+    if (tile < n_tiles_p) {
+      const int key0 = p_begin + tile * C::BN;
+      const int blk = __builtin_amdgcn_readfirstlane(ids[0]);
+      const bool inb = blk >= 0 && blk < blocks;
+      if (!inb && err && lane == 0) atomicOr(err, kErrBlockId);
+      const int64_t off = inb ? (int64_t)blk * block_bytes + head_bytes +
+                                    (int64_t)(key0 & ((1 << lg) - 1)) * C::RB
+                              : 0;
+      kb = pool_k + off;
+      vb = pool_v + off;
+      records = inb ? min(C::BN, p_end - key0) * C::RB : 0;
+      stride = C::RB;
+    } else {
+      const int s0 = (tile - n_tiles_p) * C::BN;
+      const int64_t off = ((int64_t)(q0 + s0) * H + head) * C::RB;
+      kb = ks + off;
+      vb = vs + off;
+      const int nv = min(C::BN, n_s - s0);
+      stride = H * C::RB;
+      records = nv > 0 ? (nv - 1) * stride + C::RB : 0;
+    }
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, records, kFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int voff = row[j] * stride + cb[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kl + (4 * wave + j) * 1024, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vl + (4 * wave + j) * 1024, 16, voff, 0, 0, 0);
+    }
+  }
+};
+
+struct SoftmaxState {
+  float m_run = -__builtin_inff();  // running max, log2 domain (scaled)
+  float l_run = 0.f;                // this lane-half's share of the row sum
+};
+
+__device__ __forceinline__ float max16(const f32x16 &v) {
+  // max3 tree: 8 instructions for 16 values
+  const float a = fmaxf(fmaxf(v[0], v[1]), v[2]), b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float c = fmaxf(fmaxf(v[6], v[7]), v[8]), d = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float e = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, v[15]));
+}
+
+// One key tile: S^T per 32-key block (block-major, so the softmax of a
+// block overlaps the MFMAs of the next), per-block online softmax,
+// O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *vl,
+                                             const bf16x8 (&qf)[Bf16Cfg<D>::KK],
+                                             f32x16 (&o)[Bf16Cfg<D>::ND], SoftmaxState &sm,
+                                             float cs, int valid, int lane,
+                                             const LdsOffsets<D> &lo) {
+  using C = Bf16Cfg<D>;
+  constexpr float kTau = 8.0f;  // rescale only when the max grows by > 2^8
+  const int hf = lane >> 5;
+
+  f32x16 s[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const bf16x8 a = *(const bf16x8 *)(kl + lo.k[kk] + nb * 32 * C::RB);
+      s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[nb], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    // ---- mask keys past the end of a partial tile
+    if (valid < C::BN) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * nb + 16 * (i >> 3) + 8 * hf + (i & 7);
+        if (key >= valid) s[nb][i] = -__builtin_inff();
+      }
+    }
+    // ---- online softmax over this block (row = this lane's column)
+    const float mt = row_max_both_halves(max16(s[nb])) * cs;
+    if (__any(mt > sm.m_run + kTau)) {
+      const float m_new = fmaxf(sm.m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(sm.m_run - m_new);
+      sm.l_run *= alpha;
+#pragma unroll
+      for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[nd][i] *= alpha;
+      sm.m_run = m_new;
+    }
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, -sm.m_run));
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = e[2 * i] + e[2 * i + 1];
+    sm.l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+    // ---- O^T += V^T P^T over the block's two 16-key chunks
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int kc = 2 * nb + half;
+      const int e0 = 8 * half;
+      u32x4 pw;
+      pw[0] = pack_bf16x2(e[e0 + 0], e[e0 + 1]);
+      pw[1] = pack_bf16x2(e[e0 + 2], e[e0 + 3]);
+      pw[2] = pack_bf16x2(e[e0 + 4], e[e0 + 5]);
+      pw[3] = pack_bf16x2(e[e0 + 6], e[e0 + 7]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int nd = 0; nd < C::ND; ++nd) {
+        // transpose read: group lane 4k+q loads V[key0 + k][d0 + 4q .. +3]
+        // and lane i of the group receives V[key0 + 0..3][d0 + i]
+        const v4i16 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(vl + lo.v[nd][0] + kc * 16 * C::RB));
+        const v4i16 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(vl + lo.v[nd][1] + kc * 16 * C::RB));
+        const v8i16 av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        o[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                        o[nd], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Wait for this wave's outstanding tile copies (vmcnt = 0), then barrier:
+// after it every wave's copies of the next tile have landed in LDS.
+__device__ __forceinline__ void copies_landed_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unchanged
+  __syncthreads();
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
+  // two LDS stages, K and V each a separate object, so that the compiler can
+  // tell the copy into one stage from the reads of the other and inserts no
+  // wait for the in-flight copy inside the compute
+  __shared__ __attribute__((aligned(1024))) uint8_t st0k[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0v[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1k[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1v[C::TILE];
 
   const WorkItem it = p.items[blockIdx.x];
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
@@ -142,7 +343,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
-  const int lm = tid % C::KG, lc = tid / C::KG;  // loader sub-tile
 
   // Q fragments (B operand of S^T = K Q^T): lane holds row `col`,
   // dims 16*kk + 8*hf .. +7
@@ -159,106 +359,88 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
     }
   }
 
+  TileCopy<D> cp;
+  cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
+  cp.pool_v = (const uint8_t *)p.pool_v[x.mode];
+  cp.ks = (const uint8_t *)p.k;
+  cp.vs = (const uint8_t *)p.v;
+  cp.bt_row = p.block_table + (int64_t)it.r * p.bt_stride;
+  cp.lg = p.pool_bs_log2[x.mode];
+  cp.blocks = p.pool_blocks[x.mode];
+  cp.bt_stride = p.bt_stride;
+  cp.H = p.H;
+  cp.head = head;
+  cp.q0 = x.q0;
+  // suffix rows that lie past total_s (inconsistent lengths) are never read
+  cp.n_s = (x.q0 >= 0) ? min(x.n_s, p.total_s - x.q0) : 0;
+  cp.p_begin = x.p_begin;
+  cp.p_end = x.p_end;
   const int n_pkeys = x.p_end - x.p_begin;
-  const int n_tiles_p = (n_pkeys + C::BN - 1) / C::BN;
-  const int n_tiles = n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  cp.n_tiles_p = n_pkeys > 0 ? (n_pkeys + C::BN - 1) / C::BN : 0;
+  cp.wave = wave;
+  cp.lane = lane;
+  cp.err = p.err;
+  cp.whole_blocks = (1 << cp.lg) >= C::BN;
+  cp.block_bytes = (int64_t)p.H * ((int64_t)C::RB << cp.lg);
+  cp.head_bytes = (int64_t)head * ((int64_t)C::RB << cp.lg);
+  cp.init_lanes();
+  const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  LdsOffsets<D> lo;
+  lo.init(lane);
+
+  // Rows a copy cuts off are never written; start every stage at zero so
+  // that masked keys multiply finite values.
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < C::TILE / (256 * 16); ++i) {
+      const int off = (i * 256 + tid) * 16;
+      *(u32x4 *)(st0k + off) = z;
+      *(u32x4 *)(st0v + off) = z;
+      *(u32x4 *)(st1k + off) = z;
+      *(u32x4 *)(st1v + off) = z;
+    }
+    __syncthreads();
+  }
 
   f32x16 o[C::ND];
 #pragma unroll
   for (int nd = 0; nd < C::ND; ++nd)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[nd][i] = 0.f;
-  float m_run = -__builtin_inff();  // running max, log2 domain (scaled)
-  float l_run = 0.f;                // this lane-half's share of the row sum
+  SoftmaxState sm;
   const float cs = p.scale_log2;
-  constexpr float kTau = 8.0f;      // rescale only when the max grows by > 2^8
+  auto valid_keys = [&](int t) {
+    return t < cp.n_tiles_p ? min(C::BN, n_pkeys - t * C::BN)
+                            : min(C::BN, x.n_s - (t - cp.n_tiles_p) * C::BN);
+  };
 
-  Bf16Tile T;
-  if (n_tiles > 0) bf16_load_tile<D>(p, x, it.r, head, 0, n_tiles_p, lm, lc, T);
+  int ids[4];
+  cp.load_ids(0, ids);
+  if (n_tiles > 0) cp.issue(0, ids, st0k, st0v);
+  cp.load_ids(1, ids);
+  copies_landed_barrier();  // tile 0 in LDS
 
-  for (int t = 0; t < n_tiles; ++t) {
-    uint16_t *stage = lds + (t & 1) * C::STAGE;
-    bf16_store_tile<D>(stage, lm, lc, T);
-    __syncthreads();
-    if (t + 1 < n_tiles) bf16_load_tile<D>(p, x, it.r, head, t + 1, n_tiles_p, lm, lc, T);
-
-    const uint16_t *Ks = stage;
-    const uint16_t *Vt = stage + C::K_ELEMS;
-    // ---- S^T = K Q^T
-    f32x16 s[C::NB];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const bf16x8 a = *(const bf16x8 *)(Ks + (32 * nb + col) * C::K_STRIDE + 16 * kk + 8 * hf);
-        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[nb], 0, 0, 0);
-      }
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) {
+      cp.issue(t + 1, ids, st1k, st1v);
+      cp.load_ids(t + 2, ids);
     }
-    // ---- mask keys past the end of a partial tile
-    const int valid = (t < n_tiles_p) ? min(C::BN, n_pkeys - t * C::BN)
-                                      : min(C::BN, x.n_s - (t - n_tiles_p) * C::BN);
-    if (valid < C::BN) {
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * nb + 16 * (i >> 3) + 8 * hf + (i & 7);
-          if (key >= valid) s[nb][i] = -__builtin_inff();
-        }
+    compute_tile<D>(st0k, st0v, qf, o, sm, cs, valid_keys(t), lane, lo);
+    copies_landed_barrier();  // tile t+1 landed everywhere; stage 0 free
+    if (t + 1 >= n_tiles) break;
+    if (t + 2 < n_tiles) {
+      cp.issue(t + 2, ids, st0k, st0v);
+      cp.load_ids(t + 3, ids);
     }
-    // ---- online softmax (row = this lane's column of S^T)
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * cs;
-    if (__any(mt > m_run + kTau)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int nd = 0; nd < C::ND; ++nd)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[nd][i] *= alpha;
-      m_run = m_new;
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, -m_run));
-        s[nb][i] = e;
-        lsum += e;
-      }
-    l_run += lsum;
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int kc = 0; kc < 2 * C::NB; ++kc) {
-      const f32x16 &sb = s[kc >> 1];
-      const int e0 = 8 * (kc & 1);
-      u32x4 pw;
-      pw[0] = pack_bf16x2(sb[e0 + 0], sb[e0 + 1]);
-      pw[1] = pack_bf16x2(sb[e0 + 2], sb[e0 + 3]);
-      pw[2] = pack_bf16x2(sb[e0 + 4], sb[e0 + 5]);
-      pw[3] = pack_bf16x2(sb[e0 + 6], sb[e0 + 7]);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int nd = 0; nd < C::ND; ++nd) {
-        const bf16x8 a = *(const bf16x8 *)(Vt + (32 * nd + col) * C::V_STRIDE + 16 * kc + 8 * hf);
-        o[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[nd], 0, 0, 0);
-      }
-    }
+    compute_tile<D>(st1k, st1v, qf, o, sm, cs, valid_keys(t + 1), lane, lo);
+    copies_landed_barrier();  // tile t+2 landed everywhere; stage 1 free
   }
 
   // ---- epilogue: normalise, write O (and lse) or the split partial
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sm.l_run + __shfl_xor(sm.l_run, 32);
   const float inv = 1.0f / l_tot;
-  const float lse_nat = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+  const float lse_nat = (sm.m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (!row_ok) return;
   if (x.n_chunks <= 1) {
     uint16_t *out = (uint16_t *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D;

@@ -14,12 +14,12 @@ hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t 
                        int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
                        int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
                        hipStream_t stream);
-hipError_t launch_attn_bf16(const AttnParams &p, int D, int grid, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
 hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
                             int H, int D, bool bf16, void *out, float *lse, hipStream_t stream);
-int bf16_rows_per_item(int D);
+int bf16_rows_per_item(int W);
 int bf16_keys_per_tile(int D);
 int f32_rows_per_item();
 int f32_keys_per_tile();
@@ -55,6 +55,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // A pure function of host-side bounds so that the workspace size and the
 // launch agree.
 struct Plan {
+  int waves = 4;          // bf16 kernel: waves per workgroup (32 rows each)
   int bm = 0, bn = 0;
   int chunk_len = 0;      // 0: prefixes are never split
   int max_chunks = 1;
@@ -68,7 +69,14 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
                int32_t max_p, Plan &pl) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
-  pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(D) : f32_rows_per_item();
+  // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
+  // long enough to fill them, else four (128 rows)
+  if (const char *e = std::getenv("BAT_WAVES")) {
+    pl.waves = std::atoi(e) == 8 ? 8 : 4;
+  } else {
+    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B) ? 8 : 4;
+  }
+  pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
   pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D) : f32_keys_per_tile();
   // Split a prefix only when the unsplit batch cannot fill the GPU
   // (about two items per CU on 256 CUs) and the prefix is long.
@@ -246,7 +254,7 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                   (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
                   st) != hipSuccess)
     return BAT_ERR_HIP;
-  const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, (int)pl.grid, st)
+  const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, (int)pl.grid, st)
                                       : launch_attn_f32(p, D, (int)pl.grid, st);
   if (e != hipSuccess) return BAT_ERR_HIP;
   if (pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)

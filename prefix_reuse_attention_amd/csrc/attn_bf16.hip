@@ -35,12 +35,21 @@ namespace bat {
 // every lane issues its load and masked keys hold zeros.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 
+// Workgroup shape: W waves of 32 query rows share every K/V tile; each wave
+// copies 16/W of the tile's 16 one-kilobyte pieces of K and of V.
+template <int W>
+struct WgCfg {
+  static constexpr int WAVES = W;
+  static constexpr int THREADS = 64 * W;
+  static constexpr int ROWS = 32;                   // query rows per wave
+  static constexpr int BM = W * ROWS;               // query rows per item
+  static constexpr int CPW = 16 / W;                // copy instructions per wave per tile
+};
+
+// Tile geometry (depends on the head dim only).
 template <int D>
 struct Bf16Cfg {
   static constexpr int BN = (D == 128) ? 64 : 128;  // keys per tile
-  static constexpr int WAVES = 4;
-  static constexpr int ROWS = 32;                   // query rows per wave
-  static constexpr int BM = WAVES * ROWS;           // query rows per item
   static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   static constexpr int RB = D * 2;                  // bytes per K/V row
   static constexpr int RPI = 64 / CPR;              // rows per wave copy instruction
@@ -48,7 +57,7 @@ struct Bf16Cfg {
   static constexpr int NB = BN / 32;                // 32-key MFMA blocks per tile
   static constexpr int ND = D / 32;                 // 32-wide d blocks of O
   static constexpr int KK = D / 16;                 // k-steps of QK^T
-  static_assert(TILE == 16384, "4 copy instructions per wave per tile");
+  static_assert(TILE == 16384, "16 one-kilobyte copy pieces per tile");
 };
 
 // Chunk swizzle of K/V row r: chunk c of the row is stored at c ^ swz(r).
@@ -120,41 +129,42 @@ struct LdsOffsets {
 
 // Everything one workgroup needs to copy the tiles of its item.
 //
-// Each wave issues four 16-byte-per-lane copies of K and four of V per tile;
-// copy j of wave w fills LDS bytes [(4w+j)*1024, +1024) of the stage, i.e.
-// tile row r = RPI*(4w+j) + lane/CPR, stored chunk lane%CPR, which holds the
-// row's global chunk (lane%CPR) ^ swz(r).
+// Each wave issues CPW 16-byte-per-lane copies of K and CPW of V per tile;
+// copy j of wave w fills LDS bytes [(CPW*w+j)*1024, +1024) of the stage, i.e.
+// tile row r = RPI*(CPW*w+j) + lane/CPR, stored chunk lane%CPR, which holds
+// the row's global chunk (lane%CPR) ^ swz(r).
 //
 // When a pool block holds at least one tile (block_size >= BN), a tile is
 // one contiguous run inside one block (or of the packed suffix), so the
 // copy is a buffer load: a per-tile base in SGPRs, lane-constant offsets,
 // and the descriptor's size cutting off rows past the end (they read as
 // zero).  Smaller blocks (item pools) gather per lane.
-template <int D>
+template <int D, int W>
 struct TileCopy {
   using C = Bf16Cfg<D>;
+  static constexpr int CPW = WgCfg<W>::CPW;
   const uint8_t *pool_k, *pool_v, *ks, *vs;  // prefix pool / suffix K,V bases
   const int32_t *bt_row;                     // this request's block-table row
   int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p;
   bool whole_blocks;                         // block_size >= BN
   int64_t block_bytes, head_bytes;           // H*bs*RB, head*bs*RB
   int wave, lane;
-  int row[4], cb[4];                         // tile row and stored-chunk source byte
+  int row[CPW], cb[CPW];                     // tile row and stored-chunk source byte
   int32_t *err;
 
   __device__ __forceinline__ void init_lanes() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      row[j] = C::RPI * (4 * wave + j) + lane / C::CPR;
+    for (int j = 0; j < CPW; ++j) {
+      row[j] = C::RPI * (CPW * wave + j) + lane / C::CPR;
       cb[j] = ((lane % C::CPR) ^ swz<D>(row[j])) << 4;
     }
   }
 
   // block ids of prefix tile `tile` (-1 = none): one per tile for whole
   // blocks, else one per row this lane copies
-  __device__ __forceinline__ void load_ids(int tile, int (&ids)[4]) const {
+  __device__ __forceinline__ void load_ids(int tile, int (&ids)[CPW]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CPW; ++j) {
       const int key = p_begin + tile * C::BN + (whole_blocks ? 0 : row[j]);
       const int slot = key >> lg;
       const bool ok = tile < n_tiles_p && key < p_end && slot < bt_stride &&
@@ -164,12 +174,12 @@ struct TileCopy {
   }
 
   // Issue the copy of tile `tile` into one LDS stage (K at kl, V at vl).
-  __device__ __forceinline__ void issue(int tile, const int (&ids)[4], uint8_t *kl,
+  __device__ __forceinline__ void issue(int tile, const int (&ids)[CPW], uint8_t *kl,
                                         uint8_t *vl) const {
     constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
     if (tile < n_tiles_p && !whole_blocks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < CPW; ++j) {
         const int key = p_begin + tile * C::BN + row[j];
         const int blk = ids[j];
         const bool inb = blk >= 0 && blk < blocks;
@@ -182,8 +192,8 @@ struct TileCopy {
           ksrc = pool_k + off;
           vsrc = pool_v + off;
         }
-        __builtin_amdgcn_global_load_lds(ksrc, kl + (4 * wave + j) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, vl + (4 * wave + j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ksrc, kl + (CPW * wave + j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc, vl + (CPW * wave + j) * 1024, 16, 0, 0);
       }
       return;
     }
@@ -215,10 +225,10 @@ struct TileCopy {
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CPW; ++j) {
       const int voff = row[j] * stride + cb[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kl + (4 * wave + j) * 1024, 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vl + (4 * wave + j) * 1024, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
     }
   }
 };
@@ -325,9 +335,10 @@ __device__ __forceinline__ void copies_landed_barrier() {
   __syncthreads();
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
+template <int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   using C = Bf16Cfg<D>;
+  using G = WgCfg<W>;
   // two LDS stages, K and V each a separate object, so that the compiler can
   // tell the copy into one stage from the reads of the other and inserts no
   // wait for the in-flight copy inside the compute
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
 
   // Q fragments (B operand of S^T = K Q^T): lane holds row `col`,
   // dims 16*kk + 8*hf .. +7
-  const int row = it.m_tile * C::BM + wave * C::ROWS + col;
+  const int row = it.m_tile * G::BM + wave * G::ROWS + col;
   const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
   bf16x8 qf[C::KK];
   {
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
     }
   }
 
-  TileCopy<D> cp;
+  TileCopy<D, W> cp;
   cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
   cp.pool_v = (const uint8_t *)p.pool_v[x.mode];
   cp.ks = (const uint8_t *)p.k;
@@ -393,8 +404,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < C::TILE / (256 * 16); ++i) {
-      const int off = (i * 256 + tid) * 16;
+    for (int i = 0; i < C::TILE / (G::THREADS * 16); ++i) {
+      const int off = (i * G::THREADS + tid) * 16;
       *(u32x4 *)(st0k + off) = z;
       *(u32x4 *)(st0v + off) = z;
       *(u32x4 *)(st1k + off) = z;
@@ -415,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
                             : min(C::BN, x.n_s - (t - cp.n_tiles_p) * C::BN);
   };
 
-  int ids[4];
+  int ids[G::CPW];
   cp.load_ids(0, ids);
   if (n_tiles > 0) cp.issue(0, ids, st0k, st0v);
   cp.load_ids(1, ids);
@@ -469,15 +480,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnParams p) {
   }
 }
 
-int bf16_rows_per_item(int D) { return D == 128 ? Bf16Cfg<128>::BM : Bf16Cfg<64>::BM; }
+int bf16_rows_per_item(int W) { return W == 8 ? WgCfg<8>::BM : WgCfg<4>::BM; }
 int bf16_keys_per_tile(int D) { return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN; }
 
-hipError_t launch_attn_bf16(const AttnParams &p, int D, int grid, hipStream_t stream) {
+hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
-  else if (D == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+  if (D == 128 && W == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), dim3(grid), dim3(512), 0, stream, p);
+  else if (D == 128 && W == 4)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, p);
+  else if (D == 64 && W == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), dim3(grid), dim3(512), 0, stream, p);
+  else if (D == 64 && W == 4)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), dim3(grid), dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -109,6 +109,18 @@ def test_split_prefix_merge(gpu_ready, monkeypatch, dtype, D):
     _compare_full(wl)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
+    """Both workgroup shapes (4 or 8 waves of 32 rows sharing each K/V tile)
+    on ragged suffixes, user and item prefixes, and a partial last block."""
+    monkeypatch.setenv("BAT_WAVES", waves)
+    wl = W.make_custom(dtype="bf16", H=3, D=D, n_s=[300, 17, 129, 256], n_p=[777, 64, 0, 1000],
+                       mode=[W.USER, W.ITEM, W.USER, W.ITEM], seed=100 + D, num_items=600,
+                       name=f"bf16_w{waves}_D{D}")
+    _compare_full(wl)
+
+
 def test_automatic_split_few_items(gpu_ready):
     """One request with a long prefix and a short suffix: too few items to
     fill the GPU, so the library splits the prefix by itself."""

@@ -14,7 +14,8 @@ hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t 
                        int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
                        int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
                        hipStream_t stream);
-hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, int grid, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
+                            hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
 hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
@@ -56,6 +57,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // launch agree.
 struct Plan {
   int waves = 4;          // bf16 kernel: waves per workgroup (32 rows each)
+  bool flat_gather = false;  // bf16 kernel: global instead of buffer loads for per-key gathers
   int bm = 0, bn = 0;
   int chunk_len = 0;      // 0: prefixes are never split
   int max_chunks = 1;
@@ -76,6 +78,9 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   } else {
     pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B) ? 8 : 4;
   }
+  // BAT_GATHER=flat: the per-key gather of small pool blocks always takes
+  // the global-load form that pools of 2 GiB or more need
+  if (const char *e = std::getenv("BAT_GATHER")) pl.flat_gather = std::strcmp(e, "flat") == 0;
   pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
   pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D) : f32_keys_per_tile();
   // Split a prefix only when the unsplit batch cannot fill the GPU
@@ -254,7 +259,7 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                   (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
                   st) != hipSuccess)
     return BAT_ERR_HIP;
-  const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, (int)pl.grid, st)
+  const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, pl.flat_gather, (int)pl.grid, st)
                                       : launch_attn_f32(p, D, (int)pl.grid, st);
   if (e != hipSuccess) return BAT_ERR_HIP;
   if (pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)

@@ -4,15 +4,15 @@
 // The method (Bat page, "This paper's idea"): either the user history or a
 // set of cached items is the prefix whose K/V is reused; the suffix tokens
 // are fresh and see the prefix and each other, with no positions and no
-// causal mask.  Per work item (request r, head h, a tile of 128 suffix rows,
-// a prefix chunk) one workgroup of four waves streams key tiles: first the
-// prefix tiles gathered through the block table, then the request's own
-// suffix tiles, with an online softmax.  Crossing from the prefix tiles to
+// causal mask.  Per work item (request r, head h, a tile of 32*W suffix
+// rows, a prefix chunk) one workgroup of W waves (W = 8 for long suffixes,
+// else 4) streams key tiles: first the prefix tiles gathered through the
+// block table, then the request's own suffix tiles, with an online softmax.  Crossing from the prefix tiles to
 // the suffix tiles is the log-sum-exp merge of the prefix and suffix
 // partials, done in registers.
 //
 // Data flow of one key tile (BN keys, 16 KB of K and 16 KB of V):
-//   HBM/L2 --buffer/global_load_dwordx4 ... lds--> LDS, row-major, 16-byte
+//   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS, row-major, 16-byte
 //            chunks XOR-swizzled per row (no VGPR staging, no LDS store
 //            instructions); two LDS stages, the next tile's copy in flight
 //            while the current one is consumed, one barrier per tile
@@ -31,9 +31,16 @@
 
 namespace bat {
 
-// 16 zero bytes: the copy source of keys past the end of a tile, so that
-// every lane issues its load and masked keys hold zeros.
+// 16 zero bytes: the copy source of keys past the end of a tile in the
+// global-load gather, so that every lane issues its load and masked keys
+// hold zeros.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
+
+// Pools smaller than this are gathered with buffer loads and 32-bit
+// offsets; an offset of kPastPool lies past any such pool's end, and with
+// the 16 bytes of one load added it still does not wrap.
+constexpr int64_t kBufferPoolLimit = 0x7FFFFFF0;
+constexpr int kPastPool = 0x7FFFFFF0;
 
 // Workgroup shape: W waves of 32 query rows share every K/V tile; each wave
 // copies 16/W of the tile's 16 one-kilobyte pieces of K and of V.
@@ -138,8 +145,15 @@ struct LdsOffsets {
 // one contiguous run inside one block (or of the packed suffix), so the
 // copy is a buffer load: a per-tile base in SGPRs, lane-constant offsets,
 // and the descriptor's size cutting off rows past the end (they read as
-// zero).  Smaller blocks (item pools) gather per lane.
-template <int D, int W>
+// zero).  Smaller blocks (item pools) gather per lane: a buffer load over
+// the whole pool with one 32-bit offset per lane (keys past the end get an
+// offset past the descriptor's size and read as zero), or, for a pool of
+// 2 GiB or more (FLAT), a global load per lane.  The buffer form keeps the
+// LDS-read wait counts exact: a global (FLAT-encoded) copy into LDS counts
+// on the LDS counter too, so while one can be in flight every LDS read has
+// to be waited for in full.  A block id out of range is remembered in
+// `bad` and reported once, after the loop.
+template <int D, int W, bool FLAT>
 struct TileCopy {
   using C = Bf16Cfg<D>;
   static constexpr int CPW = WgCfg<W>::CPW;
@@ -148,9 +162,10 @@ struct TileCopy {
   int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p;
   bool whole_blocks;                         // block_size >= BN
   int64_t block_bytes, head_bytes;           // H*bs*RB, head*bs*RB
+  int32_t pool_records;                      // bytes of the prefix pool (< 2 GiB unless FLAT)
   int wave, lane;
   int row[CPW], cb[CPW];                     // tile row and stored-chunk source byte
-  int32_t *err;
+  bool bad = false;                          // a block id out of range was seen
 
   __device__ __forceinline__ void init_lanes() {
 #pragma unroll
@@ -175,25 +190,32 @@ struct TileCopy {
 
   // Issue the copy of tile `tile` into one LDS stage (K at kl, V at vl).
   __device__ __forceinline__ void issue(int tile, const int (&ids)[CPW], uint8_t *kl,
-                                        uint8_t *vl) const {
+                                        uint8_t *vl) {
     constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
     if (tile < n_tiles_p && !whole_blocks) {
+      const __amdgpu_buffer_rsrc_t rpk = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)pool_k, (short)0, FLAT ? 0 : pool_records, kFlags);
+      const __amdgpu_buffer_rsrc_t rpv = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)pool_v, (short)0, FLAT ? 0 : pool_records, kFlags);
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
         const int key = p_begin + tile * C::BN + row[j];
         const int blk = ids[j];
         const bool inb = blk >= 0 && blk < blocks;
-        if (key < p_end && !inb && err) atomicOr(err, kErrBlockId);
-        const uint8_t *ksrc = (const uint8_t *)g_zero16;
-        const uint8_t *vsrc = (const uint8_t *)g_zero16;
-        if (key < p_end && inb) {
-          const int64_t off =
-              ((((int64_t)blk * H + head) << lg) | (key & ((1 << lg) - 1))) * C::RB + cb[j];
-          ksrc = pool_k + off;
-          vsrc = pool_v + off;
+        bad |= key < p_end && !inb;
+        const bool use = key < p_end && inb;
+        const int64_t off =
+            ((((int64_t)blk * H + head) << lg) | (key & ((1 << lg) - 1))) * C::RB + cb[j];
+        if constexpr (FLAT) {
+          const uint8_t *ksrc = use ? pool_k + off : (const uint8_t *)g_zero16;
+          const uint8_t *vsrc = use ? pool_v + off : (const uint8_t *)g_zero16;
+          __builtin_amdgcn_global_load_lds(ksrc, kl + (CPW * wave + j) * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc, vl + (CPW * wave + j) * 1024, 16, 0, 0);
+        } else {
+          const int voff = use ? (int)off : kPastPool;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, kl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rpv, vl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds(ksrc, kl + (CPW * wave + j) * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, vl + (CPW * wave + j) * 1024, 16, 0, 0);
       }
       return;
     }
@@ -203,7 +225,7 @@ struct TileCopy {
       const int key0 = p_begin + tile * C::BN;
       const int blk = __builtin_amdgcn_readfirstlane(ids[0]);
       const bool inb = blk >= 0 && blk < blocks;
-      if (!inb && err && lane == 0) atomicOr(err, kErrBlockId);
+      bad |= !inb;
       const int64_t off = inb ? (int64_t)blk * block_bytes + head_bytes +
                                     (int64_t)(key0 & ((1 << lg) - 1)) * C::RB
                               : 0;
@@ -335,7 +357,7 @@ __device__ __forceinline__ void copies_landed_barrier() {
   __syncthreads();
 }
 
-template <int D, int W>
+template <int D, int W, bool FLAT>
 __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   using C = Bf16Cfg<D>;
   using G = WgCfg<W>;
@@ -370,7 +392,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
     }
   }
 
-  TileCopy<D, W> cp;
+  TileCopy<D, W, FLAT> cp;
   cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
   cp.pool_v = (const uint8_t *)p.pool_v[x.mode];
   cp.ks = (const uint8_t *)p.k;
@@ -390,10 +412,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.n_tiles_p = n_pkeys > 0 ? (n_pkeys + C::BN - 1) / C::BN : 0;
   cp.wave = wave;
   cp.lane = lane;
-  cp.err = p.err;
   cp.whole_blocks = (1 << cp.lg) >= C::BN;
   cp.block_bytes = (int64_t)p.H * ((int64_t)C::RB << cp.lg);
   cp.head_bytes = (int64_t)head * ((int64_t)C::RB << cp.lg);
+  cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
   LdsOffsets<D> lo;
@@ -448,7 +470,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
     copies_landed_barrier();  // tile t+2 landed everywhere; stage 1 free
   }
 
-  // ---- epilogue: normalise, write O (and lse) or the split partial
+  // ---- epilogue: report bad block ids, normalise, write O (and lse) or the split partial
+  if (p.err && __any(cp.bad) && lane == 0) atomicOr(p.err, kErrBlockId);
   const float l_tot = sm.l_run + __shfl_xor(sm.l_run, 32);
   const float inv = 1.0f / l_tot;
   const float lse_nat = (sm.m_run + log2f(l_tot)) * 0.69314718055994530942f;
@@ -483,16 +506,29 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
 int bf16_rows_per_item(int W) { return W == 8 ? WgCfg<8>::BM : WgCfg<4>::BM; }
 int bf16_keys_per_tile(int D) { return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN; }
 
-hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, int grid, hipStream_t stream) {
+template <int D, int W>
+static void launch_one(const AttnParams &p, bool flat, int grid, hipStream_t stream) {
+  if (flat)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, true>), dim3(grid), dim3(64 * W), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, false>), dim3(grid), dim3(64 * W), 0, stream, p);
+}
+
+hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
+                            hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
+  bool flat = flat_gather;
+  for (int m = 0; m < 2; ++m)
+    flat |= (int64_t)p.pool_blocks[m] * p.H * ((int64_t)2 * D << p.pool_bs_log2[m]) >
+            kBufferPoolLimit;
   if (D == 128 && W == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), dim3(grid), dim3(512), 0, stream, p);
+    launch_one<128, 8>(p, flat, grid, stream);
   else if (D == 128 && W == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, p);
+    launch_one<128, 4>(p, flat, grid, stream);
   else if (D == 64 && W == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), dim3(grid), dim3(512), 0, stream, p);
+    launch_one<64, 8>(p, flat, grid, stream);
   else if (D == 64 && W == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), dim3(grid), dim3(256), 0, stream, p);
+    launch_one<64, 4>(p, flat, grid, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

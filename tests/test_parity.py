@@ -57,9 +57,13 @@ def test_bf16_ragged_mixed(gpu_ready, D):
     _compare_full(wl)
 
 
+@pytest.mark.parametrize("gather", ["buffer", "flat"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_bf16_small_blocks(gpu_ready, D):
-    """User pools with 1-, 2- and 16-token pages (the per-key gather path)."""
+def test_bf16_small_blocks(gpu_ready, monkeypatch, D, gather):
+    """User pools with 1-, 2- and 16-token pages (the per-key gather path),
+    in both gather forms: buffer loads with 32-bit offsets into the pool and
+    the global loads that pools of 2 GiB or more take."""
+    monkeypatch.setenv("BAT_GATHER", gather)
     for bs in (1, 2, 16):
         wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=[40, 3], n_p=[77, 130],
                            mode=[W.USER, W.USER], seed=40 + bs, user_block_size=bs,

@@ -45,6 +45,42 @@ def measured_traffic(config, per_launch_units):
     return s.get("hbm_bytes_per_launch")
 
 
+def _pmc_kib(run_dir, counter, name_part):
+    """Mean per-dispatch value (KiB) of one counter over the dispatches of
+    kernels whose name contains name_part, from a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} values for '{name_part}' under {run_dir}")
+    return sum(per.values()) / len(per)
+
+
+def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of the
+    benchmark and of --copy-calibration) into the HBM-traffic summary that
+    the roofline record quotes: counter KiB scaled by what the same counter
+    reads for a plain copy of known size."""
+    n_kib = (1 << 30) / 1024.0
+    f_scale = n_kib / _pmc_kib(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    w_scale = n_kib / _pmc_kib(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f = _pmc_kib(fetch_dir, "FETCH_SIZE", "attn_bf16_kernel")
+    w = _pmc_kib(write_dir, "WRITE_SIZE", "attn_bf16_kernel")
+    summary = {"kernel": "attn_bf16_kernel", "config": config,
+               "kernel_source_hash": kernel_source_hash(),
+               "fetch_kib": f, "write_kib": w, "fetch_scale": f_scale, "write_scale": w_scale,
+               "hbm_bytes_per_launch": (f * f_scale + w * w_scale) * 1024.0}
+    with open(PMC_SUMMARY, "w") as fh:
+        json.dump(summary, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(summary), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -56,7 +92,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the "
                          "HBM byte counters of rocprofv3 --pmc)")
+    ap.add_argument("--write-traffic-summary", nargs=4,
+                    metavar=("FETCH_RUN", "WRITE_RUN", "COPY_FETCH_RUN", "COPY_WRITE_RUN"),
+                    help="write the committed HBM-traffic summary from four rocprofv3 --pmc "
+                         "output directories (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic_summary:
+        write_traffic_summary(*args.write_traffic_summary, config=f"config{args.config}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by request with no exchange; see the design notes)",
@@ -167,8 +210,10 @@ def main():
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": "attn_bf16_kernel<128>" if (bf16 and wl.D == 128) else
-                               ("attn_bf16_kernel<64>" if bf16 else f"attn_f32_kernel<{wl.D}>"),
+                     # bf16: D, waves per workgroup (8 when suffixes average >= 192
+                     # rows, as the library chooses), global-load gathers (pools >= 2 GiB)
+                     "kernel": (f"attn_bf16_kernel<{wl.D}, {8 if wl.total_s >= 192 * wl.B else 4}, false>"
+                                if bf16 else f"attn_f32_kernel<{wl.D}>"),
                      "kernel_ms_mean": round(kernel_ms, 5)},
         "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
                      "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),

@@ -159,7 +159,7 @@ struct TileCopy {
   static constexpr int CPW = WgCfg<W>::CPW;
   const uint8_t *pool_k, *pool_v, *ks, *vs;  // prefix pool / suffix K,V bases
   const int32_t *bt_row;                     // this request's block-table row
-  int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p;
+  int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p, n_tiles;
   bool whole_blocks;                         // block_size >= BN
   int64_t block_bytes, head_bytes;           // H*bs*RB, head*bs*RB
   int32_t pool_records;                      // bytes of the prefix pool (< 2 GiB unless FLAT)
@@ -188,15 +188,29 @@ struct TileCopy {
     }
   }
 
-  // Issue the copy of tile `tile` into one LDS stage (K at kl, V at vl).
-  __device__ __forceinline__ void issue(int tile, const int (&ids)[CPW], uint8_t *kl,
-                                        uint8_t *vl) {
+  // Where the 2*CPW copy instructions of one tile read from: a buffer
+  // descriptor per tensor and a byte offset per lane (FLAT gathers: an
+  // address per lane).  Planning is separate from issuing so that the
+  // instructions can be spread over the MFMAs of the previous tile: issued
+  // together by all waves they queue at the texture unit and stall every
+  // wave's in-order issue.  A tile past the last plans zero-size copies.
+  struct Plan {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int voff[CPW];
+    const uint8_t *ksrc[FLAT ? CPW : 1], *vsrc[FLAT ? CPW : 1];
+    bool flat_gather;
+  };
+
+  __device__ __forceinline__ Plan plan(int tile, const int (&ids)[CPW]) {
     constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
+    Plan pl;
+    pl.flat_gather = false;
     if (tile < n_tiles_p && !whole_blocks) {
-      const __amdgpu_buffer_rsrc_t rpk = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)pool_k, (short)0, FLAT ? 0 : pool_records, kFlags);
-      const __amdgpu_buffer_rsrc_t rpv = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)pool_v, (short)0, FLAT ? 0 : pool_records, kFlags);
+      pl.flat_gather = FLAT;
+      pl.rk = __builtin_amdgcn_make_buffer_rsrc((void *)pool_k, (short)0,
+                                                FLAT ? 0 : pool_records, kFlags);
+      pl.rv = __builtin_amdgcn_make_buffer_rsrc((void *)pool_v, (short)0,
+                                                FLAT ? 0 : pool_records, kFlags);
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
         const int key = p_begin + tile * C::BN + row[j];
@@ -206,18 +220,13 @@ struct TileCopy {
         const bool use = key < p_end && inb;
         const int64_t off =
             ((((int64_t)blk * H + head) << lg) | (key & ((1 << lg) - 1))) * C::RB + cb[j];
+        pl.voff[j] = use ? (int)off : kPastPool;
         if constexpr (FLAT) {
-          const uint8_t *ksrc = use ? pool_k + off : (const uint8_t *)g_zero16;
-          const uint8_t *vsrc = use ? pool_v + off : (const uint8_t *)g_zero16;
-          __builtin_amdgcn_global_load_lds(ksrc, kl + (CPW * wave + j) * 1024, 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vsrc, vl + (CPW * wave + j) * 1024, 16, 0, 0);
-        } else {
-          const int voff = use ? (int)off : kPastPool;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, kl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rpv, vl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
+          pl.ksrc[j] = use ? pool_k + off : (const uint8_t *)g_zero16;
+          pl.vsrc[j] = use ? pool_v + off : (const uint8_t *)g_zero16;
         }
       }
-      return;
+      return pl;
     }
     const uint8_t *kb, *vb;
     int records, stride;
@@ -234,24 +243,40 @@ struct TileCopy {
       records = inb ? min(C::BN, p_end - key0) * C::RB : 0;
       stride = C::RB;
     } else {
-      const int s0 = (tile - n_tiles_p) * C::BN;
+      const int s0 = max(tile - n_tiles_p, 0) * C::BN;
       const int64_t off = ((int64_t)(q0 + s0) * H + head) * C::RB;
       kb = ks + off;
       vb = vs + off;
-      const int nv = min(C::BN, n_s - s0);
+      const int nv = tile < n_tiles ? min(C::BN, n_s - s0) : 0;
       stride = H * C::RB;
       records = nv > 0 ? (nv - 1) * stride + C::RB : 0;
     }
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, records, kFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
+    pl.rk = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, records, kFlags);
+    pl.rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int voff = row[j] * stride + cb[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vl + (CPW * wave + j) * 1024, 16, voff, 0, 0, 0);
-    }
+    for (int j = 0; j < CPW; ++j) pl.voff[j] = row[j] * stride + cb[j];
+    return pl;
+  }
+
+  // Copy instruction j of 2*CPW (K pieces first, then V) into the stage at
+  // kl / vl.
+  __device__ __forceinline__ void fire(const Plan &pl, int j, uint8_t *kl, uint8_t *vl) const {
+    const bool is_v = j >= CPW;
+    const int q = is_v ? j - CPW : j;
+    uint8_t *dst = (is_v ? vl : kl) + (CPW * wave + q) * 1024;
+    if (FLAT && pl.flat_gather)
+      __builtin_amdgcn_global_load_lds(is_v ? pl.vsrc[FLAT ? q : 0] : pl.ksrc[FLAT ? q : 0], dst,
+                                       16, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? pl.rv : pl.rk, dst, 16, pl.voff[q], 0, 0, 0);
+  }
+
+  // Issue the whole copy of tile `tile` into one stage at once.
+  __device__ __forceinline__ void issue(int tile, const int (&ids)[CPW], uint8_t *kl,
+                                        uint8_t *vl) {
+    const Plan pl = plan(tile, ids);
+#pragma unroll
+    for (int j = 0; j < 2 * CPW; ++j) fire(pl, j, kl, vl);
   }
 };
 
@@ -268,86 +293,136 @@ __device__ __forceinline__ float max16(const f32x16 &v) {
   return fmaxf(fmaxf(fmaxf(a, b), fmaxf(c, d)), fmaxf(e, v[15]));
 }
 
-// One key tile: S^T per 32-key block (block-major, so the softmax of a
-// block overlaps the MFMAs of the next), per-block online softmax,
-// O^T += V^T P^T.
-template <int D>
+// One key tile: S^T, then per 32-key block the online softmax and
+// O^T += V^T P^T.  hook(i) runs after S^T MFMA i.  Every LDS operand is read two MFMAs ahead of its use
+// (hard scheduling barriers keep the compiler from moving the reads back
+// next to their MFMAs, where each would wait out the full LDS latency),
+// and the first two V operands of a block are read before its softmax so
+// that they arrive during the exponentials.
+template <int D, typename Hook>
 __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *vl,
                                              const bf16x8 (&qf)[Bf16Cfg<D>::KK],
                                              f32x16 (&o)[Bf16Cfg<D>::ND], SoftmaxState &sm,
                                              float cs, int valid, int lane,
-                                             const LdsOffsets<D> &lo) {
+                                             const LdsOffsets<D> &lo, Hook &&hook) {
   using C = Bf16Cfg<D>;
   constexpr float kTau = 8.0f;  // rescale only when the max grows by > 2^8
+  constexpr int NS = C::NB * C::KK;  // MFMAs of S^T
+  constexpr int NV = 2 * C::ND;      // PV MFMAs per 32-key block
   const int hf = lane >> 5;
 
+  // ---- S^T: MFMA i accumulates block i % NB, k-step i / NB, so that
+  // consecutive MFMAs are independent
+  auto kread = [&](int i) __attribute__((always_inline)) {
+    return *(const bf16x8 *)(kl + lo.k[i / C::NB] + (i % C::NB) * 32 * C::RB);
+  };
   f32x16 s[C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
+  for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
+  bf16x8 a[3];
+  a[0] = kread(0);
+  a[1] = kread(1);
 #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      const bf16x8 a = *(const bf16x8 *)(kl + lo.k[kk] + nb * 32 * C::RB);
-      s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[nb], 0, 0, 0);
-    }
+  for (int i = 0; i < NS; ++i) {
+    if (i + 2 < NS) a[(i + 2) % 3] = kread(i + 2);
+    s[i % C::NB] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], qf[i / C::NB], s[i % C::NB], 0, 0, 0);
+    hook(i);  // the caller's copy instructions, spread over the S^T MFMAs
+    __builtin_amdgcn_sched_barrier(0);
   }
 
+  // PV operand j of block nb: 16-key chunk 2nb + j / ND, d block j % ND,
+  // two transpose reads (group lane 4k+q loads V[key0 + k][d0 + 4q .. +3]
+  // and lane i of the group receives V[key0 + 0..3][d0 + i])
+  auto vread = [&](int nb, int j) __attribute__((always_inline)) {
+    const int kc = 2 * nb + j / C::ND, nd = j % C::ND;
+    const v4i16 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(vl + lo.v[nd][0] + kc * 16 * C::RB));
+    const v4i16 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(vl + lo.v[nd][1] + kc * 16 * C::RB));
+    const v8i16 av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    return __builtin_bit_cast(bf16x8, av);
+  };
+
+  // ---- one row maximum for the whole tile (keys past a partial tile's
+  // end are -inf first), and the lazy rescale it may call for
+  bf16x8 b[3];
+  b[0] = vread(0, 0);
+  b[1] = vread(0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (valid < C::BN) {
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    // ---- mask keys past the end of a partial tile
-    if (valid < C::BN) {
+    for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = 32 * nb + 16 * (i >> 3) + 8 * hf + (i & 7);
         if (key >= valid) s[nb][i] = -__builtin_inff();
       }
-    }
-    // ---- online softmax over this block (row = this lane's column)
-    const float mt = row_max_both_halves(max16(s[nb])) * cs;
-    if (__any(mt > sm.m_run + kTau)) {
-      const float m_new = fmaxf(sm.m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(sm.m_run - m_new);
-      sm.l_run *= alpha;
+  }
+  float mloc = max16(s[0]);
 #pragma unroll
-      for (int nd = 0; nd < C::ND; ++nd)
+  for (int nb = 1; nb < C::NB; ++nb) mloc = fmaxf(mloc, max16(s[nb]));
+  const float mt = row_max_both_halves(mloc) * cs;
+  if (__any(mt > sm.m_run + kTau)) {
+    const float m_new = fmaxf(sm.m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(sm.m_run - m_new);
+    sm.l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[nd][i] *= alpha;
-      sm.m_run = m_new;
-    }
-    float e[16];
+    for (int nd = 0; nd < C::ND; ++nd)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, -sm.m_run));
-    float t8[8];
+      for (int i = 0; i < 16; ++i) o[nd][i] *= alpha;
+    sm.m_run = m_new;
+  }
+  const float nm = -sm.m_run;
+
+  // probabilities p = 2^(s*cs - m) of block nb, elements i, i+1 (this
+  // lane-half's share of the row sum goes to la / lb), packed to bf16 in
+  // the PV B operand words
+  u32x4 pw[C::NB][2];
+  float la = 0.f, lb = 0.f;
+  auto probs2 = [&](int nb, int i) __attribute__((always_inline)) {
+    float x0 = s[nb][i], x1 = s[nb][i + 1];
+    asm volatile("" : "+v"(x0), "+v"(x1));
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, cs, nm));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, cs, nm));
+    la += p0;
+    lb += p1;
+    uint32_t w = pack_bf16x2(p0, p1);
+    asm volatile("" : "+v"(w), "+v"(la), "+v"(lb));
+    pw[nb][i >> 3][(i & 7) >> 1] = w;
+  };
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t8[i] = e[2 * i] + e[2 * i + 1];
-    sm.l_run += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
-    // ---- O^T += V^T P^T over the block's two 16-key chunks
+  for (int i = 0; i < 16; i += 2) probs2(0, i);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- O^T += V^T P^T block by block; the MFMAs of block nb carry the
+  // exponentials of block nb+1 between them
+  constexpr int PPS = 16 / NV;  // probabilities of the next block per PV MFMA
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kc = 2 * nb + half;
-      const int e0 = 8 * half;
-      u32x4 pw;
-      pw[0] = pack_bf16x2(e[e0 + 0], e[e0 + 1]);
-      pw[1] = pack_bf16x2(e[e0 + 2], e[e0 + 3]);
-      pw[2] = pack_bf16x2(e[e0 + 4], e[e0 + 5]);
-      pw[3] = pack_bf16x2(e[e0 + 6], e[e0 + 7]);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pw[nb][0]);
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, pw[nb][1]);
 #pragma unroll
-      for (int nd = 0; nd < C::ND; ++nd) {
-        // transpose read: group lane 4k+q loads V[key0 + k][d0 + 4q .. +3]
-        // and lane i of the group receives V[key0 + 0..3][d0 + i]
-        const v4i16 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16 *)(vl + lo.v[nd][0] + kc * 16 * C::RB));
-        const v4i16 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16 *)(vl + lo.v[nd][1] + kc * 16 * C::RB));
-        const v8i16 av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        o[nd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
-                                                        o[nd], 0, 0, 0);
+    for (int j = 0; j < NV; ++j) {
+      // operand reads run two MFMAs ahead, across block boundaries; the
+      // three operand registers rotate on the tile-wide MFMA index g
+      const int g = nb * NV + j, jn = j + 2;
+      if (jn < NV)
+        b[(g + 2) % 3] = vread(nb, jn);
+      else if (nb + 1 < C::NB)
+        b[(g + 2) % 3] = vread(nb + 1, jn - NV);
+      o[j % C::ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[g % 3], j < C::ND ? pb0 : pb1,
+                                                             o[j % C::ND], 0, 0, 0);
+      if (nb + 1 < C::NB) {
+#pragma unroll
+        for (int q = 0; q < PPS; q += 2) probs2(nb + 1, PPS * j + q);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  sm.l_run += la + lb;
 }
 
 // Wait for this wave's outstanding tile copies (vmcnt = 0), then barrier:
@@ -418,6 +493,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  cp.n_tiles = n_tiles;
   LdsOffsets<D> lo;
   lo.init(lane);
 
@@ -454,20 +530,23 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.load_ids(1, ids);
   copies_landed_barrier();  // tile 0 in LDS
 
+  // Tile t is consumed from one stage while the copy of tile t+1 into the
+  // other goes out one instruction every SPACING S^T MFMAs (a tile past the
+  // last copies nothing).
+  constexpr int SPACING = (C::NB * C::KK) / (2 * G::CPW);
+  auto tile_step = [&](int t, uint8_t *kc, uint8_t *vc, uint8_t *kn, uint8_t *vn)
+      __attribute__((always_inline)) {
+    const auto pl = cp.plan(t + 1, ids);
+    cp.load_ids(t + 2, ids);
+    compute_tile<D>(kc, vc, qf, o, sm, cs, valid_keys(t), lane, lo, [&](int i) {
+      if (i % SPACING == 0) cp.fire(pl, i / SPACING, kn, vn);
+    });
+    copies_landed_barrier();  // tile t+1 landed everywhere; this stage free
+  };
   for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) {
-      cp.issue(t + 1, ids, st1k, st1v);
-      cp.load_ids(t + 2, ids);
-    }
-    compute_tile<D>(st0k, st0v, qf, o, sm, cs, valid_keys(t), lane, lo);
-    copies_landed_barrier();  // tile t+1 landed everywhere; stage 0 free
+    tile_step(t, st0k, st0v, st1k, st1v);
     if (t + 1 >= n_tiles) break;
-    if (t + 2 < n_tiles) {
-      cp.issue(t + 2, ids, st0k, st0v);
-      cp.load_ids(t + 3, ids);
-    }
-    compute_tile<D>(st1k, st1v, qf, o, sm, cs, valid_keys(t + 1), lane, lo);
-    copies_landed_barrier();  // tile t+2 landed everywhere; stage 1 free
+    tile_step(t + 1, st1k, st1v, st0k, st0v);
   }
 
   // ---- epilogue: report bad block ids, normalise, write O (and lse) or the split partial

@@ -104,7 +104,8 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   const int64_t n_groups = (int64_t)H * B * pl.max_chunks;
   pl.grid = kNumXcd * ((n_groups + kNumXcd - 1) / kNumXcd) * t_max;
   pl.part_rows = pl.max_chunks > 1 ? (int64_t)pl.max_chunks * total_s : 0;
-  if (pl.grid > (int64_t)1 << 30) return false;
+  // the planner counts items and split-partial rows in 32 bits
+  if (pl.grid > (int64_t)1 << 30 || pl.part_rows >= (int64_t)1 << 31) return false;
   size_t off = align256(kHdrWords * sizeof(int32_t));
   pl.off_items = off;    off = align256(off + sizeof(WorkItem) * (size_t)pl.grid);
   pl.off_meta = off;     off = align256(off + sizeof(ReqMeta) * (size_t)B);

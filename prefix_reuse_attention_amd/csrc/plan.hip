@@ -8,30 +8,31 @@
 // largest per-item key count first) and dealt round-robin over the XCDs, so
 // each XCD's queue also runs longest first, which bounds the tail.
 //
-// One workgroup of 1024 threads; thread t owns a contiguous run of requests,
+// One workgroup of 256 threads; thread t owns a contiguous run of requests,
 // and every prefix sum over requests is a block-wide scan (wave shuffles,
-// then one pass over the 16 wave totals).
+// then one pass over the four wave totals).  All counts fit in 32 bits: the
+// host bounds the item grid and the split-partial rows below 2^31.
 #include "common.h"
 
 namespace bat {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kPlanLds = 4096;  // batches up to this size keep per-request state in LDS
 
-// Exclusive block-wide scan of NV int64 lanes per thread; returns totals.
+// Exclusive block-wide scan of NV lanes per thread; returns the totals.
 template <int NV>
-__device__ __forceinline__ void block_scan(int64_t (&v)[NV], int64_t (&total)[NV],
-                                           int64_t (*s_wave)[kNumXcd], int64_t *s_total) {
+__device__ __forceinline__ void block_scan(int32_t (&v)[NV], int32_t (&total)[NV],
+                                           int32_t (*s_wave)[kNumXcd], int32_t *s_total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int64_t inc[NV];
+  int32_t inc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) inc[i] = v[i];
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int64_t t = __shfl_up(inc[i], off);
+      const int32_t t = __shfl_up(inc[i], off);
       if (lane >= off) inc[i] += t;
     }
   }
@@ -40,9 +41,10 @@ __device__ __forceinline__ void block_scan(int64_t (&v)[NV], int64_t (&total)[NV
     for (int i = 0; i < NV; ++i) s_wave[w][i] = inc[i];
   __syncthreads();
   if (tid < NV) {
-    int64_t acc = 0;
+    int32_t acc = 0;
+#pragma unroll
     for (int j = 0; j < kPlanWaves; ++j) {
-      const int64_t t = s_wave[j][tid];
+      const int32_t t = s_wave[j][tid];
       s_wave[j][tid] = acc;
       acc += t;
     }
@@ -63,8 +65,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
     ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
   const int tid = threadIdx.x;
-  __shared__ int64_t s_wave[kPlanWaves][kNumXcd];
-  __shared__ int64_t s_total[kNumXcd];
+  __shared__ int32_t s_wave[kPlanWaves][kNumXcd];
+  __shared__ int32_t s_total[kNumXcd];
   __shared__ int32_t s_req[4 * kPlanLds];
   // per request: work key, sorted order, suffix length, chunk count
   int32_t *base = B <= kPlanLds ? s_req : g_scratch;
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
           *req_nc = base + 3 * stride;
 
   if (tid == 0) hdr[kHdrError] = 0;
-  for (int64_t idx = tid; idx < grid; idx += kPlanThreads) items[idx] = WorkItem{-1, 0, 0, 0};
+  for (int idx = tid; idx < grid; idx += kPlanThreads) items[idx] = WorkItem{-1, 0, 0, 0};
 
   const int per = (B + kPlanThreads - 1) / kPlanThreads;
   const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   // 1) per request: chunks, work key (keys per item), split-partial rows;
   //    partial offsets are an exclusive scan in request order
   {
-    int64_t part[1] = {0}, tot[1];
+    int32_t part[1] = {0}, tot[1];
     for (int r = k0; r < k1; ++r) {
       const int n_s = cu_s[r + 1] - cu_s[r];
       const int n_p = min(max(prefix_lens[r], 0), max_p);
@@ -90,13 +92,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       req_nc[r] = nc;
       req_ns[r] = n_s;
       req_key[r] = (n_s > 0) ? (nc > 1 ? chunk_len : n_p) + n_s : -1;
-      if (nc > 1 && n_s > 0) part[0] += (int64_t)nc * n_s;
+      if (nc > 1 && n_s > 0) part[0] += nc * n_s;
     }
     block_scan<1>(part, tot, s_wave, s_total);
     for (int r = k0; r < k1; ++r) {
       const int nc = req_nc[r], n_s = req_ns[r];
-      meta[r] = ReqMeta{nc, (int32_t)part[0]};
-      if (nc > 1 && n_s > 0) part[0] += (int64_t)nc * n_s;
+      meta[r] = ReqMeta{nc, part[0]};
+      if (nc > 1 && n_s > 0) part[0] += nc * n_s;
     }
   }
   __syncthreads();
@@ -112,31 +114,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
   __syncthreads();
   // 3) groups of my run of sorted requests, and the first global group index
-  int64_t g0[1] = {0}, ng_total[1];
+  int32_t g0[1] = {0}, ng_total[1];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
-    if (req_ns[r] > 0) g0[0] += (int64_t)H * req_nc[r];
+    if (req_ns[r] > 0) g0[0] += H * req_nc[r];
   }
   block_scan<1>(g0, ng_total, s_wave, s_total);
   // 4) slots each XCD gives my groups: group g goes to XCD g % 8
-  int64_t slots[kNumXcd] = {0, 0, 0, 0, 0, 0, 0, 0}, used[kNumXcd];
-  int64_t g = g0[0];
+  int32_t slots[kNumXcd] = {0, 0, 0, 0, 0, 0, 0, 0}, used[kNumXcd];
+  int32_t g = g0[0];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
     const int n_s = req_ns[r];
     if (n_s <= 0) continue;
     const int T = (n_s + bm - 1) / bm;
-    const int64_t ng = (int64_t)H * req_nc[r];
+    const int ng = H * req_nc[r];
 #pragma unroll
     for (int x = 0; x < kNumXcd; ++x) {
-      const int64_t first = g + ((x - g % kNumXcd) + kNumXcd) % kNumXcd;
-      const int64_t cnt = first < g + ng ? (g + ng - 1 - first) / kNumXcd + 1 : 0;
+      const int first = g + ((x - g % kNumXcd) + kNumXcd) % kNumXcd;
+      const int cnt = first < g + ng ? (g + ng - 1 - first) / kNumXcd + 1 : 0;
       slots[x] += cnt * T;
     }
     g += ng;
   }
   block_scan<kNumXcd>(slots, used, s_wave, s_total);
-  // 5) write my items
+  // 5) write my items (heads fastest within a request's groups, then chunks)
   g = g0[0];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
@@ -144,23 +146,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     if (n_s <= 0) continue;
     const int T = (n_s + bm - 1) / bm;
     const int nc = req_nc[r];
-    const int64_t ng = (int64_t)H * nc;
-    for (int64_t gi = 0; gi < ng; ++gi, ++g) {
-      const int x = (int)(g % kNumXcd);
-      const int h = (int)(gi % H), c = (int)(gi / H);
+    int h = 0, c = 0;
+    for (int gi = 0; gi < H * nc; ++gi, ++g) {
+      const int x = g % kNumXcd;
       for (int t = 0; t < T; ++t) {
-        const int64_t idx = (slots[x] + t) * kNumXcd + x;
+        const int idx = (slots[x] + t) * kNumXcd + x;
         if (idx < grid) items[idx] = WorkItem{r, h, t, c};
         else atomicOr(&hdr[kHdrError], kErrLength);  // grid bound too small
       }
       slots[x] += T;
+      if (++h == H) {
+        h = 0;
+        ++c;
+      }
     }
   }
   if (tid == 0) {
-    int64_t n = 0;
+    int32_t n = 0;
 #pragma unroll
     for (int x = 0; x < kNumXcd; ++x) n += used[x];
-    hdr[kHdrItems] = (int32_t)n;
+    hdr[kHdrItems] = n;
   }
 }
 

@@ -324,6 +324,9 @@ __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *v
   bf16x8 a[3];
   a[0] = kread(0);
   a[1] = kread(1);
+  // MFMA runs at raised wave priority: while this wave issues MFMAs, the
+  // other wave on the SIMD fills the gaps with its vector work
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     if (i + 2 < NS) a[(i + 2) % 3] = kread(i + 2);
@@ -332,6 +335,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *v
     hook(i);  // the caller's copy instructions, spread over the S^T MFMAs
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // PV operand j of block nb: 16-key chunk 2nb + j / ND, d block j % ND,
   // two transpose reads (group lane 4k+q loads V[key0 + k][d0 + 4q .. +3]
@@ -400,6 +404,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *v
   // ---- O^T += V^T P^T block by block; the MFMAs of block nb carry the
   // exponentials of block nb+1 between them
   constexpr int PPS = 16 / NV;  // probabilities of the next block per PV MFMA
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     const bf16x8 pb0 = __builtin_bit_cast(bf16x8, pw[nb][0]);
@@ -422,6 +427,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *v
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   sm.l_run += la + lb;
 }
 
@@ -457,15 +463,6 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   const int row = it.m_tile * G::BM + wave * G::ROWS + col;
   const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
   bf16x8 qf[C::KK];
-  {
-    const uint16_t *q = (const uint16_t *)p.q + ((int64_t)(x.q0 + row) * p.H + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok) w = *(const u32x4 *)(q + 16 * kk + 8 * hf);
-      qf[kk] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
 
   TileCopy<D, W, FLAT> cp;
   cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
@@ -497,21 +494,6 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   LdsOffsets<D> lo;
   lo.init(lane);
 
-  // Rows a copy cuts off are never written; start every stage at zero so
-  // that masked keys multiply finite values.
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < C::TILE / (G::THREADS * 16); ++i) {
-      const int off = (i * G::THREADS + tid) * 16;
-      *(u32x4 *)(st0k + off) = z;
-      *(u32x4 *)(st0v + off) = z;
-      *(u32x4 *)(st1k + off) = z;
-      *(u32x4 *)(st1v + off) = z;
-    }
-    __syncthreads();
-  }
-
   f32x16 o[C::ND];
 #pragma unroll
   for (int nd = 0; nd < C::ND; ++nd)
@@ -524,11 +506,23 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
                             : min(C::BN, x.n_s - (t - cp.n_tiles_p) * C::BN);
   };
 
+  // Every copy writes its whole stage (lanes past the end of the data write
+  // zeros), so the stages need no clearing.  The Q loads go out between the
+  // block-id load of tile 0 and its copy, so that the latencies overlap.
   int ids[G::CPW];
   cp.load_ids(0, ids);
-  if (n_tiles > 0) cp.issue(0, ids, st0k, st0v);
+  {
+    const uint16_t *q = (const uint16_t *)p.q + ((int64_t)(x.q0 + row) * p.H + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok) w = *(const u32x4 *)(q + 16 * kk + 8 * hf);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  cp.issue(0, ids, st0k, st0v);
   cp.load_ids(1, ids);
-  copies_landed_barrier();  // tile 0 in LDS
+  copies_landed_barrier();  // tile 0 in LDS, Q in registers
 
   // Tile t is consumed from one stage while the copy of tile t+1 into the
   // other goes out one instruction every SPACING S^T MFMAs (a tile past the

@@ -163,6 +163,17 @@ struct TileCopy {
   bool whole_blocks;                         // block_size >= BN
   int64_t block_bytes, head_bytes;           // H*bs*RB, head*bs*RB
   int32_t pool_records;                      // bytes of the prefix pool (< 2 GiB unless FLAT)
+  // Per-item table of whole-tile copies: for tile u (a prefix tile of a
+  // pool whose blocks hold whole tiles, or a suffix tile) the K source
+  // address, byte count and row stride; its V source is the K address plus
+  // dv_p (prefix) or dv_s (suffix).  Filled once per item by all threads,
+  // it replaces the per-tile block-id load and address arithmetic that
+  // every wave would otherwise repeat.  Items of more tiles, and per-key
+  // gather tiles, plan each tile as it comes.
+  static constexpr int kTabTiles = 512;
+  u32x4 *tab;
+  bool use_tab;
+  int64_t dv_p, dv_s;
   int wave, lane;
   int row[CPW], cb[CPW];                     // tile row and stored-chunk source byte
   bool bad = false;                          // a block id out of range was seen
@@ -178,6 +189,7 @@ struct TileCopy {
   // block ids of prefix tile `tile` (-1 = none): one per tile for whole
   // blocks, else one per row this lane copies
   __device__ __forceinline__ void load_ids(int tile, int (&ids)[CPW]) const {
+    if (use_tab && whole_blocks) return;  // the table holds the block ids
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int key = p_begin + tile * C::BN + (whole_blocks ? 0 : row[j]);
@@ -201,10 +213,56 @@ struct TileCopy {
     bool flat_gather;
   };
 
+  // Fill the table (thread tid of nthreads); the caller waits for the LDS
+  // stores and meets the other waves at a barrier before the first plan.
+  __device__ __forceinline__ void fill_tab(int tid, int nthreads) {
+    for (int u = tid; u < n_tiles; u += nthreads) {
+      const uint8_t *addr = pool_k;
+      int records = 0, stride = C::RB;
+      if (u < n_tiles_p) {
+        if (whole_blocks) {
+          const int key0 = p_begin + u * C::BN;
+          const int slot = key0 >> lg;
+          const int blk = slot < bt_stride ? bt_row[slot] : -1;
+          const bool inb = blk >= 0 && blk < blocks;
+          bad |= !inb;
+          if (inb) {
+            addr = pool_k + (int64_t)blk * block_bytes + head_bytes +
+                   (int64_t)(key0 & ((1 << lg) - 1)) * C::RB;
+            records = min(C::BN, p_end - key0) * C::RB;
+          }
+        }
+      } else {
+        const int s0 = (u - n_tiles_p) * C::BN;
+        addr = ks + ((int64_t)(q0 + s0) * H + head) * C::RB;
+        stride = H * C::RB;
+        const int nv = min(C::BN, n_s - s0);
+        records = nv > 0 ? (nv - 1) * stride + C::RB : 0;
+      }
+      const uint64_t a = (uint64_t)addr;
+      tab[u] = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)records, (uint32_t)stride};
+    }
+  }
+
   __device__ __forceinline__ Plan plan(int tile, const int (&ids)[CPW]) {
     constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
     Plan pl;
     pl.flat_gather = false;
+    if (use_tab && (tile >= n_tiles_p || whole_blocks)) {
+      // whole-tile copy from the table (a tile past the last copies nothing)
+      const u32x4 e = tile < n_tiles ? tab[tile] : u32x4{0u, 0u, 0u, 0u};
+      const uint64_t a = ((uint64_t)__builtin_amdgcn_readfirstlane(e[1]) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane(e[0]);
+      const int records = __builtin_amdgcn_readfirstlane(e[2]);
+      const int stride = __builtin_amdgcn_readfirstlane(e[3]);
+      const uint8_t *kb = (const uint8_t *)a;
+      const uint8_t *vb = kb + (tile < n_tiles_p ? dv_p : dv_s);
+      pl.rk = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, records, kFlags);
+      pl.rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) pl.voff[j] = row[j] * stride + cb[j];
+      return pl;
+    }
     if (tile < n_tiles_p && !whole_blocks) {
       pl.flat_gather = FLAT;
       pl.rk = __builtin_amdgcn_make_buffer_rsrc((void *)pool_k, (short)0,
@@ -491,6 +549,16 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
   cp.n_tiles = n_tiles;
+  __shared__ u32x4 s_tab[TileCopy<D, W, FLAT>::kTabTiles];
+  cp.tab = s_tab;
+  cp.use_tab = n_tiles <= TileCopy<D, W, FLAT>::kTabTiles;
+  cp.dv_p = cp.pool_v - cp.pool_k;
+  cp.dv_s = cp.vs - cp.ks;
+  if (cp.use_tab) {
+    cp.fill_tab(tid, G::THREADS);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
+    __syncthreads();                     // every entry visible
+  }
   LdsOffsets<D> lo;
   lo.init(lane);
 

@@ -125,6 +125,17 @@ def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
     _compare_full(wl)
 
 
+@pytest.mark.parametrize("D,n_p", [(128, 40000), (64, 70000)])
+def test_bf16_long_unsplit_prefix(gpu_ready, monkeypatch, D, n_p):
+    """An item of more than 512 key tiles (a chunk length beyond the prefix
+    keeps it whole): its copies are planned tile by tile instead of from the
+    per-item table."""
+    monkeypatch.setenv("BAT_SPLIT_CHUNK", "1000000")
+    wl = W.make_custom(dtype="bf16", H=1, D=D, n_s=[70, 3], n_p=[n_p, 500],
+                       mode=[W.USER, W.USER], seed=95 + D, name=f"long_unsplit_D{D}")
+    _compare_full(wl)
+
+
 def test_automatic_split_few_items(gpu_ready):
     """One request with a long prefix and a short suffix: too few items to
     fill the GPU, so the library splits the prefix by itself."""

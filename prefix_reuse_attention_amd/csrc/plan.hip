@@ -59,20 +59,23 @@ __device__ __forceinline__ void block_scan(int32_t (&v)[NV], int32_t (&total)[NV
   __syncthreads();  // s_wave / s_total are reused by the next scan
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+// The planner body, with the per-request arrays (work key, sorted order,
+// suffix length, chunk count) at req[0 .. 4*stride): in LDS for batches up
+// to kPlanLds requests, else in the global scratch.  The two cases are
+// separate instances so that LDS accesses compile to LDS instructions (a
+// generic pointer would make every access wait for global memory too).
+template <typename ReqPtr>
+__device__ __forceinline__ void plan_body(
     const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
     int32_t B, int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-    int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
-    ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
+    ReqPtr req, int32_t stride, int32_t (*s_wave)[kNumXcd], int32_t *s_total,
+    __attribute__((address_space(3))) int32_t *fast, ReqMeta *__restrict__ meta,
+    WorkItem *__restrict__ items, int32_t *hdr) {
   const int tid = threadIdx.x;
-  __shared__ int32_t s_wave[kPlanWaves][kNumXcd];
-  __shared__ int32_t s_total[kNumXcd];
-  __shared__ int32_t s_req[4 * kPlanLds];
-  // per request: work key, sorted order, suffix length, chunk count
-  int32_t *base = B <= kPlanLds ? s_req : g_scratch;
-  const int32_t stride = B <= kPlanLds ? kPlanLds : B;
-  int32_t *req_key = base, *req_order = base + stride, *req_ns = base + 2 * stride,
-          *req_nc = base + 3 * stride;
+  ReqPtr req_key = req, req_order = req + stride, req_ns = req + 2 * stride,
+         req_nc = req + 3 * stride;
 
   if (tid == 0) hdr[kHdrError] = 0;
   for (int idx = tid; idx < grid; idx += kPlanThreads) items[idx] = WorkItem{-1, 0, 0, 0};
@@ -138,7 +141,52 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     g += ng;
   }
   block_scan<kNumXcd>(slots, used, s_wave, s_total);
-  // 5) write my items (heads fastest within a request's groups, then chunks)
+  // 5) write the items (heads fastest within a request's groups, then chunks).
+  // The j-th group of sorted request k that lands on XCD x takes slots
+  // base_k(x) + j*T_k .. +T_k-1 there, base_k(x) being the per-XCD scan above.
+  if (B <= kPlanThreads) {
+    // One request per thread: publish each request's bases, first group,
+    // row-tile count and item offset, then every thread writes items,
+    // finding an item's request by binary search over the offsets.
+    lds_i32 *s_base = fast, *s_g0 = fast + kNumXcd * kPlanThreads,
+            *s_T = s_g0 + kPlanThreads, *s_r = s_T + kPlanThreads, *s_off = s_r + kPlanThreads;
+    int32_t nit[1] = {0}, total[1];
+    int T = 0, r = -1;
+    if (tid < B) {
+      r = req_order[tid];
+      const int n_s = req_ns[r];
+      if (n_s > 0) {
+        T = (n_s + bm - 1) / bm;
+        nit[0] = H * req_nc[r] * T;
+      }
+    }
+    block_scan<1>(nit, total, s_wave, s_total);
+    if (tid < B) {
+#pragma unroll
+      for (int x = 0; x < kNumXcd; ++x) s_base[tid * kNumXcd + x] = slots[x];
+      s_g0[tid] = g0[0];
+      s_T[tid] = T;
+      s_r[tid] = r;
+      s_off[tid] = nit[0];
+    }
+    __syncthreads();
+    for (int i = tid; i < total[0]; i += kPlanThreads) {
+      int lo = 0, hi = B - 1;  // the last request whose items start at or before i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const int k = lo, Tk = s_T[k], G0 = s_g0[k];
+      const int local = i - s_off[k];
+      const int gi = local / Tk, t = local - gi * Tk;
+      const int x = (G0 + gi) % kNumXcd;
+      const int first = ((x - G0 % kNumXcd) + kNumXcd) % kNumXcd;
+      const int idx = (s_base[k * kNumXcd + x] + ((gi - first) / kNumXcd) * Tk + t) * kNumXcd + x;
+      if (idx < grid) items[idx] = WorkItem{s_r[k], gi % H, t, gi / H};
+      else atomicOr(&hdr[kHdrError], kErrLength);  // grid bound too small
+    }
+  } else {
   g = g0[0];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
@@ -161,12 +209,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       }
     }
   }
+  }
   if (tid == 0) {
     int32_t n = 0;
 #pragma unroll
     for (int x = 0; x < kNumXcd; ++x) n += used[x];
     hdr[kHdrItems] = n;
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
+    int32_t B, int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
+    int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
+    ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
+  __shared__ int32_t s_wave[kPlanWaves][kNumXcd];
+  __shared__ int32_t s_total[kNumXcd];
+  __shared__ int32_t s_req[4 * kPlanLds];
+  __shared__ int32_t s_fast[(kNumXcd + 4) * kPlanThreads];
+  if (B <= kPlanLds)
+    plan_body(cu_s, prefix_lens, B, H, bm, chunk_len, max_p, grid, (lds_i32 *)s_req, kPlanLds,
+              s_wave, s_total, (lds_i32 *)s_fast, meta, items, hdr);
+  else
+    plan_body(cu_s, prefix_lens, B, H, bm, chunk_len, max_p, grid, g_scratch, B, s_wave,
+              s_total, (lds_i32 *)s_fast, meta, items, hdr);
 }
 
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,

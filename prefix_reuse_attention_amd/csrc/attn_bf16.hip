@@ -7,9 +7,14 @@
 // causal mask.  Per work item (request r, head h, a tile of 32*W suffix
 // rows, a prefix chunk) one workgroup of W waves (W = 8 for long suffixes,
 // else 4) streams key tiles: first the prefix tiles gathered through the
-// block table, then the request's own suffix tiles, with an online softmax.  Crossing from the prefix tiles to
-// the suffix tiles is the log-sum-exp merge of the prefix and suffix
-// partials, done in registers.
+// block table, then the request's own suffix tiles, with an online softmax.
+// Crossing from the prefix tiles to the suffix tiles is the log-sum-exp
+// merge of the prefix and suffix partials, done in registers.
+//
+// Two kernels: attn_bf16_kernel, where every wave runs S^T, softmax and PV
+// of each tile in turn, and attn_bf16_pp_kernel (head dim 128, eight
+// waves), where two groups of four waves alternate between the MFMA work
+// and the softmax so that each SIMD always holds one wave of each kind.
 //
 // Data flow of one key tile (BN keys, 16 KB of K and 16 KB of V):
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS, row-major, 16-byte
@@ -28,6 +33,8 @@
 // both accumulators, so P never leaves registers and the per-row rescale
 // is a per-lane multiply.
 #include "common.h"
+
+#include <utility>
 
 namespace bat {
 
@@ -644,6 +651,375 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   }
 }
 
+template <typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+// f(integral_constant<int, j>) for j = 0 .. N-1, each a separate compile-time instance
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong (D = 128, W = 8).  Waves w and w+4 share a SIMD; waves 0-3 form
+// group A and waves 4-7 group B.  Every tile step has two phases with a workgroup
+// barrier between them, and in each phase one group issues MFMAs while the
+// other runs its softmax, so that each SIMD holds one wave of each kind and
+// the vector work of one passes under the MFMAs of the other:
+//   step t, phase 1:  A: O += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T
+//                     B: softmax of S(t-1); copies of K(t+1) and V(t)
+//   step t, phase 2:  A: softmax of S(t)
+//                     B: O += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T
+// K(t) and V(t) sit in stage t % 2.  The copy of K(t+1) replaces K(t-1) and
+// that of V(t) replaces V(t-2), both last read in step t-1; they land before
+// the barrier that ends step t.  Group B issues every copy, spread over its
+// softmax.  For head dim 64 (128-key tiles, twice the exponentials per MFMA)
+// the softmax outweighs the MFMAs and the kernel above serves instead.
+template <int D, bool FLAT>
+__global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
+  using C = Bf16Cfg<D>;
+  using TC = TileCopy<D, 4, FLAT>;  // group B's four waves copy every tile
+  constexpr int CPW = TC::CPW;
+  constexpr int NS = C::NB * C::KK;
+  constexpr int NV = 2 * C::ND;
+  constexpr int NPV = C::NB * NV;
+  constexpr float kTauSum = 256.0f;  // largest kept share of a block's row sum
+  constexpr int BM = 256;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1[C::TILE];
+  __shared__ u32x4 s_tab[TC::kTabTiles];
+
+  const WorkItem it = p.items[blockIdx.x];
+  if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
+  const ItemRange x = item_range(p, it);
+  const int head = it.h;
+  const int tid = threadIdx.x;
+  // the wave index as a scalar, so that the compiler sees branches on the
+  // group as uniform
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hf = lane >> 5;
+  const bool grp_a = wave < 4;
+
+  const int row = it.m_tile * BM + wave * 32 + col;
+  const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
+  bf16x8 qf[C::KK];
+
+  TC cp;
+  cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
+  cp.pool_v = (const uint8_t *)p.pool_v[x.mode];
+  cp.ks = (const uint8_t *)p.k;
+  cp.vs = (const uint8_t *)p.v;
+  cp.bt_row = p.block_table + (int64_t)it.r * p.bt_stride;
+  cp.lg = p.pool_bs_log2[x.mode];
+  cp.blocks = p.pool_blocks[x.mode];
+  cp.bt_stride = p.bt_stride;
+  cp.H = p.H;
+  cp.head = head;
+  cp.q0 = x.q0;
+  cp.n_s = (x.q0 >= 0) ? min(x.n_s, p.total_s - x.q0) : 0;
+  cp.p_begin = x.p_begin;
+  cp.p_end = x.p_end;
+  const int n_pkeys = x.p_end - x.p_begin;
+  cp.n_tiles_p = n_pkeys > 0 ? (n_pkeys + C::BN - 1) / C::BN : 0;
+  cp.wave = wave & 3;
+  cp.lane = lane;
+  cp.whole_blocks = (1 << cp.lg) >= C::BN;
+  cp.block_bytes = (int64_t)p.H * ((int64_t)C::RB << cp.lg);
+  cp.head_bytes = (int64_t)head * ((int64_t)C::RB << cp.lg);
+  cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
+  cp.init_lanes();
+  const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  cp.n_tiles = n_tiles;
+  cp.tab = s_tab;
+  cp.use_tab = n_tiles <= TC::kTabTiles;
+  cp.dv_p = cp.pool_v - cp.pool_k;
+  cp.dv_s = cp.vs - cp.ks;
+  if (cp.use_tab) {
+    cp.fill_tab(tid, 512);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
+    __syncthreads();                     // every entry visible
+  }
+  LdsOffsets<D> lo;
+  lo.init(lane);
+
+  f32x16 o[C::ND];
+#pragma unroll
+  for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[nd][i] = 0.f;
+  // running max (log2 domain): finite before the first key, so that the
+  // first tile's probabilities overflow to +inf and take the rescale path
+  // (-inf would make masked keys NaN); la: this lane-half's row-sum share
+  float m_run = -1e30f, la = 0.f;
+  f32x16 s[C::NB];
+  u32x4 pw[C::NB][2];
+  const float cs = p.scale_log2;
+  auto valid_keys = [&](int t) __attribute__((always_inline)) {
+    return t < cp.n_tiles_p ? min(C::BN, n_pkeys - t * C::BN)
+                            : min(C::BN, x.n_s - (t - cp.n_tiles_p) * C::BN);
+  };
+
+  auto kread = [&](const uint8_t *kl, int i) __attribute__((always_inline)) {
+    return *(const bf16x8 *)(kl + lo.k[i / C::NB] + (i % C::NB) * 32 * C::RB);
+  };
+  auto vread = [&](const uint8_t *vl, int i) __attribute__((always_inline)) {
+    const int nb = i / NV, j = i % NV;
+    const int kc = 2 * nb + j / C::ND, nd = j % C::ND;
+    const v4i16 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(vl + lo.v[nd][0] + kc * 16 * C::RB));
+    const v4i16 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(vl + lo.v[nd][1] + kc * 16 * C::RB));
+    const v8i16 av = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    return __builtin_bit_cast(bf16x8, av);
+  };
+
+  // The MFMA phase: O += V(t-1)^T P(t-1)^T (when PV), then S(t)^T, operand
+  // reads two MFMAs ahead through three rotating registers.
+  auto gemm = [&](const uint8_t *kt, const uint8_t *vp, auto pv_c) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_c)::value;
+    constexpr int N0 = PV ? NPV : 0, N = N0 + NS;
+    auto op = [&](int j) __attribute__((always_inline)) {
+      return j < N0 ? vread(vp, j) : kread(kt, j - N0);
+    };
+    bf16x8 r[3];
+    r[0] = op(0);
+    r[1] = op(1);
+    const f32x16 zero = {};
+    static_for<N>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j + 2 < N) r[(j + 2) % 3] = op(j + 2);
+      if constexpr (j < N0) {
+        constexpr int nb = j / NV, jj = j % NV;
+        o[jj % C::ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            r[j % 3], __builtin_bit_cast(bf16x8, pw[nb][jj / C::ND]), o[jj % C::ND], 0, 0, 0);
+      } else {
+        constexpr int i = j - N0;
+        s[i % C::NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            r[j % 3], qf[i / C::NB], i < C::NB ? zero : s[i % C::NB], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // The softmax phase for tile t.  The probabilities are taken against the
+  // running max m_run with no row maximum on the common path: a 32-key
+  // block is kept when no lane's share of its row sum exceeds 2^8, which
+  // bounds every probability by 2^8 (the lazy-rescale bound).  Otherwise
+  // (always on an item's first tile, rarely later) the tile's row maximum
+  // is taken, O and l are rescaled and the tile's probabilities recomputed.
+  // hook(k) runs after pair k (group B issues its copies there).
+  auto softmax = [&](int t, auto &&hook) __attribute__((always_inline)) {
+    const int valid = valid_keys(t);
+    if (valid < C::BN) {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * nb + 16 * (i >> 3) + 8 * hf + (i & 7);
+          if (key >= valid) s[nb][i] = -__builtin_inff();
+        }
+    }
+    float bl[C::NB];
+    auto probs = [&](float nm, bool with_hook) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = 2 * q;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], cs, nm));
+          sa += p0;
+          sb += p1;
+          pw[nb][i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+          if (with_hook) hook(8 * nb + q);
+        }
+        bl[nb] = sa + sb;
+      }
+    };
+    probs(-m_run, true);
+    bool over = false;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) over |= !(bl[nb] <= kTauSum);
+    if (__any(over)) {
+      float mloc = max16(s[0]);
+#pragma unroll
+      for (int nb = 1; nb < C::NB; ++nb) mloc = fmaxf(mloc, max16(s[nb]));
+      const float mt = row_max_both_halves(mloc) * cs;
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      la *= alpha;
+#pragma unroll
+      for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[nd][i] *= alpha;
+      m_run = m_new;
+      probs(-m_run, false);
+    }
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) la += bl[nb];
+  };
+  auto mid_barrier = []() __attribute__((always_inline)) {
+    // no memory fence: group B's copies stay in flight across it
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: Q, the copy of K(0) (group B), barrier
+  int ids[CPW];
+  typename TC::Plan pl_v;  // the plan of the tile whose V goes out next
+  {
+    const uint16_t *q = (const uint16_t *)p.q + ((int64_t)(x.q0 + row) * p.H + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok) w = *(const u32x4 *)(q + 16 * kk + 8 * hf);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  if (!grp_a) {
+    cp.load_ids(0, ids);
+    pl_v = cp.plan(0, ids);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) cp.fire(pl_v, j, k0, v0);
+    cp.load_ids(1, ids);
+  }
+  copies_landed_barrier();
+
+  auto pv_only = [&](const uint8_t *vl) __attribute__((always_inline)) {
+    bf16x8 r[3];
+    r[0] = vread(vl, 0);
+    r[1] = vread(vl, 1);
+    static_for<NPV>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j + 2 < NPV) r[(j + 2) % 3] = vread(vl, j + 2);
+      constexpr int nb = j / NV, jj = j % NV;
+      o[jj % C::ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          r[j % 3], __builtin_bit_cast(bf16x8, pw[nb][jj / C::ND]), o[jj % C::ND], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Each group runs its own copy of the whole tile loop (a separate
+  // instance, so that neither carries the other's registers).
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr bool A = decltype(role_c)::value;
+    // step 0: no PV yet
+    if constexpr (A) {
+      gemm(k0, v1, std::integral_constant<bool, false>{});
+      mid_barrier();
+      softmax(0, [](int) {});
+    } else {
+      {
+        const auto pk = cp.plan(1, ids);
+        cp.load_ids(2, ids);
+#pragma unroll
+        for (int j = 0; j < 2 * CPW; ++j) cp.fire(j < CPW ? pk : pl_v, j, k1, v0);
+        pl_v = pk;
+      }
+      mid_barrier();
+      gemm(k0, v1, std::integral_constant<bool, false>{});
+    }
+    copies_landed_barrier();
+
+    // steps 1 .. n-1: kt = K(t), vp = V(t-1), kc / vc = copy targets of
+    // K(t+1) / V(t)
+    auto step = [&](int t, const uint8_t *kt, const uint8_t *vp, uint8_t *kc, uint8_t *vc)
+        __attribute__((always_inline)) {
+      if constexpr (A) {
+        gemm(kt, vp, std::integral_constant<bool, true>{});
+        mid_barrier();
+        softmax(t, [](int) {});
+      } else {
+        const auto pk = cp.plan(t + 1, ids);
+        cp.load_ids(t + 2, ids);
+        constexpr int EVERY = (8 * C::NB) / (2 * CPW);
+        softmax(t - 1, [&](int k) __attribute__((always_inline)) {
+          if (k % EVERY == EVERY - 1) {
+            const int j = k / EVERY;
+            __builtin_amdgcn_sched_barrier(0);
+            cp.fire(j < CPW ? pk : pl_v, j, kc, vc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+        pl_v = pk;
+        mid_barrier();
+        gemm(kt, vp, std::integral_constant<bool, true>{});
+      }
+      copies_landed_barrier();
+    };
+    int t = 1;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, k1, v0, k0, v1);
+      step(t + 1, k0, v1, k1, v0);
+    }
+    if (t < n_tiles) step(t, k1, v0, k0, v1);
+
+    // tail: the last tile's PV (group A), its softmax then PV (group B)
+    const int tl = n_tiles - 1;
+    if constexpr (A) {
+      if (tl & 1) pv_only(v1); else pv_only(v0);
+      mid_barrier();
+    } else {
+      softmax(tl, [](int) {});
+      mid_barrier();
+      if (tl & 1) pv_only(v1); else pv_only(v0);
+    }
+  };
+  if (grp_a)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
+
+  // ---- epilogue: report bad block ids, normalise, write O (and lse) or the split partial
+  if (p.err && __any(cp.bad) && lane == 0) atomicOr(p.err, kErrBlockId);
+  const float l_tot = la + __shfl_xor(la, 32);
+  const float inv = 1.0f / l_tot;
+  const float lse_nat = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  if (!row_ok) return;
+  if (x.n_chunks <= 1) {
+    uint16_t *out = (uint16_t *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D;
+#pragma unroll
+    for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[nd][4 * j + 0] * inv, o[nd][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(o[nd][4 * j + 2] * inv, o[nd][4 * j + 3] * inv);
+        *(u32x2 *)(out + 32 * nd + 8 * j + 4 * hf) = w;
+      }
+    if (p.lse && hf == 0) p.lse[(int64_t)head * p.total_s + x.q0 + row] = lse_nat;
+  } else {
+    const int64_t pr = (int64_t)x.part_off + (int64_t)it.chunk * x.n_s + row;
+    float *po = p.part_o + (pr * p.H + head) * D;
+#pragma unroll
+    for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 w = {o[nd][4 * j] * inv, o[nd][4 * j + 1] * inv, o[nd][4 * j + 2] * inv,
+                   o[nd][4 * j + 3] * inv};
+        *(f32x4 *)(po + 32 * nd + 8 * j + 4 * hf) = w;
+      }
+    if (hf == 0) p.part_lse[pr * p.H + head] = lse_nat;
+  }
+}
+
+// Explicit instantiations of every kernel launched below (two kernel
+// templates that share device helpers otherwise lose one set of host stubs).
+template __global__ void attn_bf16_kernel<128, 4, false>(AttnParams);
+template __global__ void attn_bf16_kernel<128, 4, true>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 4, false>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 4, true>(AttnParams);
+template __global__ void attn_bf16_pp_kernel<128, false>(AttnParams);
+template __global__ void attn_bf16_pp_kernel<128, true>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 8, false>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 8, true>(AttnParams);
+
 int bf16_rows_per_item(int W) { return W == 8 ? WgCfg<8>::BM : WgCfg<4>::BM; }
 int bf16_keys_per_tile(int D) { return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN; }
 
@@ -655,6 +1031,14 @@ static void launch_one(const AttnParams &p, bool flat, int grid, hipStream_t str
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, false>), dim3(grid), dim3(64 * W), 0, stream, p);
 }
 
+template <int D>
+static void launch_pp(const AttnParams &p, bool flat, int grid, hipStream_t stream) {
+  if (flat)
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), dim3(grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, false>), dim3(grid), dim3(512), 0, stream, p);
+}
+
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
                             hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
@@ -663,7 +1047,7 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
     flat |= (int64_t)p.pool_blocks[m] * p.H * ((int64_t)2 * D << p.pool_bs_log2[m]) >
             kBufferPoolLimit;
   if (D == 128 && W == 8)
-    launch_one<128, 8>(p, flat, grid, stream);
+    launch_pp<128>(p, flat, grid, stream);
   else if (D == 128 && W == 4)
     launch_one<128, 4>(p, flat, grid, stream);
   else if (D == 64 && W == 8)

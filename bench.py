@@ -61,6 +61,17 @@ def _pmc_kib(run_dir, counter, name_part):
     return sum(per.values()) / len(per)
 
 
+def bf16_kernel_label(wl):
+    """The bf16 kernel the library launches for this workload: eight waves
+    (256 rows per item) when suffixes average at least 192 rows, else four;
+    with eight waves and head dim 128 the ping-pong kernel.  Buffer-load
+    gathers (pools under 2 GiB)."""
+    waves = 8 if wl.total_s >= 192 * wl.B else 4
+    if waves == 8 and wl.D == 128:
+        return "attn_bf16_pp_kernel<128, false>"
+    return f"attn_bf16_kernel<{wl.D}, {waves}, false>"
+
+
 def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of the
     benchmark and of --copy-calibration) into the HBM-traffic summary that
@@ -69,9 +80,9 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
     n_kib = (1 << 30) / 1024.0
     f_scale = n_kib / _pmc_kib(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     w_scale = n_kib / _pmc_kib(copy_write_dir, "WRITE_SIZE", "copyBuffer")
-    f = _pmc_kib(fetch_dir, "FETCH_SIZE", "attn_bf16_kernel")
-    w = _pmc_kib(write_dir, "WRITE_SIZE", "attn_bf16_kernel")
-    summary = {"kernel": "attn_bf16_kernel", "config": config,
+    f = _pmc_kib(fetch_dir, "FETCH_SIZE", "attn_bf16")
+    w = _pmc_kib(write_dir, "WRITE_SIZE", "attn_bf16")
+    summary = {"kernel": "attn_bf16", "config": config,
                "kernel_source_hash": kernel_source_hash(),
                "fetch_kib": f, "write_kib": w, "fetch_scale": f_scale, "write_scale": w_scale,
                "hbm_bytes_per_launch": (f * f_scale + w * w_scale) * 1024.0}
@@ -210,10 +221,7 @@ def main():
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     # bf16: D, waves per workgroup (8 when suffixes average >= 192
-                     # rows, as the library chooses), global-load gathers (pools >= 2 GiB)
-                     "kernel": (f"attn_bf16_kernel<{wl.D}, {8 if wl.total_s >= 192 * wl.B else 4}, false>"
-                                if bf16 else f"attn_f32_kernel<{wl.D}>"),
+                     "kernel": bf16_kernel_label(wl) if bf16 else f"attn_f32_kernel<{wl.D}>",
                      "kernel_ms_mean": round(kernel_ms, 5)},
         "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
                      "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),

@@ -185,7 +185,14 @@ struct TileCopy {
   int row[CPW], cb[CPW];                     // tile row and stored-chunk source byte
   bool bad = false;                          // a block id out of range was seen
 
+  // LDS byte offset of this wave's first piece in a stage
+  uint32_t wofs;
+  // keeps wofs from being folded into per-piece constants that are then
+  // held (or spilled) across the tile loop: called once per tile
+  __device__ __forceinline__ void anchor() { asm volatile("" : "+s"(wofs)); }
+
   __device__ __forceinline__ void init_lanes() {
+    wofs = CPW * wave * 1024;
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       row[j] = C::RPI * (CPW * wave + j) + lane / C::CPR;
@@ -323,12 +330,36 @@ struct TileCopy {
     return pl;
   }
 
+  // The table entry of tile `tile` (zeros past the last tile); read a step
+  // ahead of plan_tab so that its LDS latency is hidden.
+  __device__ __forceinline__ u32x4 tab_entry(int tile) const {
+    return tile < n_tiles ? tab[tile] : u32x4{0u, 0u, 0u, 0u};
+  }
+  // The plan of a whole-tile copy from its table entry (items whose tiles
+  // all come from the table: use_tab and whole_blocks).
+  __device__ __forceinline__ Plan plan_tab(int tile, const u32x4 &e) const {
+    constexpr int kFlags = 0x00020000;  // raw buffer, 32-bit dword format
+    Plan pl;
+    pl.flat_gather = false;
+    const uint64_t a = ((uint64_t)__builtin_amdgcn_readfirstlane(e[1]) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane(e[0]);
+    const int records = __builtin_amdgcn_readfirstlane(e[2]);
+    const int stride = __builtin_amdgcn_readfirstlane(e[3]);
+    const uint8_t *kb = (const uint8_t *)a;
+    const uint8_t *vb = kb + (tile < n_tiles_p ? dv_p : dv_s);
+    pl.rk = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, records, kFlags);
+    pl.rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, records, kFlags);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) pl.voff[j] = row[j] * stride + cb[j];
+    return pl;
+  }
+
   // Copy instruction j of 2*CPW (K pieces first, then V) into the stage at
   // kl / vl.
   __device__ __forceinline__ void fire(const Plan &pl, int j, uint8_t *kl, uint8_t *vl) const {
     const bool is_v = j >= CPW;
     const int q = is_v ? j - CPW : j;
-    uint8_t *dst = (is_v ? vl : kl) + (CPW * wave + q) * 1024;
+    uint8_t *dst = (is_v ? vl : kl) + wofs + q * 1024;
     if (FLAT && pl.flat_gather)
       __builtin_amdgcn_global_load_lds(is_v ? pl.vsrc[FLAT ? q : 0] : pl.ksrc[FLAT ? q : 0], dst,
                                        16, 0, 0);
@@ -907,8 +938,24 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
 
   // Each group runs its own copy of the whole tile loop (a separate
   // instance, so that neither carries the other's registers).
-  auto run = [&](auto role_c) __attribute__((always_inline)) {
+  auto run = [&](auto role_c, auto tab_c) __attribute__((always_inline)) {
     constexpr bool A = decltype(role_c)::value;
+    // group B on an item whose tiles all come from the table plans from the
+    // table alone (fewer live scalars than the general plan)
+    constexpr bool TAB = decltype(tab_c)::value;
+    u32x4 e_next = {0u, 0u, 0u, 0u};
+    if constexpr (!A && TAB) e_next = cp.tab_entry(2);
+    auto plan_next = [&](int tile) __attribute__((always_inline)) {
+      if constexpr (TAB) {
+        const auto pl = cp.plan_tab(tile, e_next);
+        e_next = cp.tab_entry(tile + 1);
+        return pl;
+      } else {
+        const auto pl = cp.plan(tile, ids);
+        cp.load_ids(tile + 1, ids);
+        return pl;
+      }
+    };
     // step 0: no PV yet
     if constexpr (A) {
       gemm(k0, v1, std::integral_constant<bool, false>{});
@@ -916,8 +963,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
       softmax(0, [](int) {});
     } else {
       {
-        const auto pk = cp.plan(1, ids);
-        cp.load_ids(2, ids);
+        const auto pk = TAB ? cp.plan_tab(1, cp.tab_entry(1)) : cp.plan(1, ids);
+        if constexpr (!TAB) cp.load_ids(2, ids);
 #pragma unroll
         for (int j = 0; j < 2 * CPW; ++j) cp.fire(j < CPW ? pk : pl_v, j, k1, v0);
         pl_v = pk;
@@ -936,8 +983,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
         mid_barrier();
         softmax(t, [](int) {});
       } else {
-        const auto pk = cp.plan(t + 1, ids);
-        cp.load_ids(t + 2, ids);
+        cp.anchor();
+        const auto pk = plan_next(t + 1);
         constexpr int EVERY = (8 * C::NB) / (2 * CPW);
         softmax(t - 1, [&](int k) __attribute__((always_inline)) {
           if (k % EVERY == EVERY - 1) {
@@ -972,9 +1019,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
     }
   };
   if (grp_a)
-    run(std::integral_constant<bool, true>{});
+    run(std::integral_constant<bool, true>{}, std::integral_constant<bool, false>{});
+  else if (cp.use_tab && cp.whole_blocks)
+    run(std::integral_constant<bool, false>{}, std::integral_constant<bool, true>{});
   else
-    run(std::integral_constant<bool, false>{});
+    run(std::integral_constant<bool, false>{}, std::integral_constant<bool, false>{});
 
   // ---- epilogue: report bad block ids, normalise, write O (and lse) or the split partial
   if (p.err && __any(cp.bad) && lane == 0) atomicOr(p.err, kErrBlockId);

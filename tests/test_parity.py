@@ -125,6 +125,22 @@ def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
     _compare_full(wl)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_tile_counts(gpu_ready, monkeypatch, D):
+    """Items of 1 to 6 key tiles with eight waves per workgroup (the
+    head-dim-128 kernel alternates two wave groups over a two-phase step, with
+    a prologue tile and a last-tile tail): every count of steps around the
+    loop's unrolling, full and partial last tiles, prefix-only and
+    suffix-only tiles."""
+    monkeypatch.setenv("BAT_WAVES", "8")
+    bn = 64 if D == 128 else 128
+    n_s = [bn, bn - 7, 2 * bn, 3, bn + 1, 2 * bn - 1]
+    n_p = [0, bn, 2 * bn - 5, 2 * bn, 3 * bn + 9, 3 * bn]
+    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s, n_p=n_p, mode=[W.USER] * 6,
+                       seed=170 + D, user_block_size=64, name=f"bf16_tiles_D{D}")
+    _compare_full(wl)
+
+
 @pytest.mark.parametrize("D,n_p", [(128, 40000), (64, 70000)])
 def test_bf16_long_unsplit_prefix(gpu_ready, monkeypatch, D, n_p):
     """An item of more than 512 key tiles (a chunk length beyond the prefix

@@ -487,8 +487,9 @@ __device__ __forceinline__ void compute_tile(const uint8_t *kl, const uint8_t *v
     asm volatile("" : "+v"(x0), "+v"(x1));
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, cs, nm));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, cs, nm));
-    la += p0;
-    lb += p1;
+    const bool first = nb == 0 && i == 0;  // the sums start at this pair
+    la = first ? p0 : la + p0;
+    lb = first ? p1 : lb + p1;
     uint32_t w = pack_bf16x2(p0, p1);
     asm volatile("" : "+v"(w), "+v"(la), "+v"(lb));
     pw[nb][i >> 3][(i & 7) >> 1] = w;
@@ -858,14 +859,14 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
     auto probs = [&](float nm, bool with_hook) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        float sa = 0.f, sb = 0.f;
+        float sa, sb;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int i = 2 * q;
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, nm));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i + 1], cs, nm));
-          sa += p0;
-          sb += p1;
+          sa = q ? sa + p0 : p0;
+          sb = q ? sb + p1 : p1;
           pw[nb][i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
           if (with_hook) hook(8 * nb + q);
         }

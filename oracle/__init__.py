@@ -155,6 +155,43 @@ def prefill_suffix(q, k_s, v_s, cu_s, k_p, v_p, cu_p, scale, rows=None,
     return out, lse
 
 
+def _no_prefix(q, B):
+    """An empty cached prefix for every request: zero key rows, zero lengths."""
+    x = np.ascontiguousarray(q)
+    empty = np.zeros((0,) + x.shape[1:], dtype=x.dtype if x.dtype in (np.uint16, np.float32)
+                     else np.float64)
+    return empty, np.zeros(B + 1, np.int32)
+
+
+def prefix_rows(q_p, k_p, v_p, cu_p, scale, rows=None, heads=None):
+    """Prefix rows of the bipartite mask, batched over packed [tokens, H, D].
+
+    Request r's prefix tokens are rows cu_p[r]:cu_p[r+1]; each such row sees
+    exactly the prefix tokens of its own request (never the suffix).  That is
+    a row group attending to itself with nothing cached before it, so the
+    batched prefill above with an empty prefix computes it.  Returns
+    (out, lse) shaped as prefill_suffix's.
+    """
+    cu_p = np.ascontiguousarray(cu_p, dtype=np.int32)
+    empty, zeros = _no_prefix(q_p, cu_p.shape[0] - 1)
+    return prefill_suffix(q_p, k_p, v_p, cu_p, empty, empty, zeros, scale, rows, heads)
+
+
+def item_local(q, k, v, tokens_per_item, scale, rows=None, heads=None):
+    """Per-item prefix rows: item i owns rows i*T .. i*T+T-1 (T =
+    tokens_per_item) of packed [n_items*T, H, D], and each of them sees only
+    its own item's T tokens (the block-diagonal form).  Returns (out, lse)
+    shaped as prefill_suffix's.
+    """
+    n = np.asarray(q).shape[0]
+    T = int(tokens_per_item)
+    if T <= 0 or n % T:
+        raise ValueError("rows must be a whole number of items")
+    cu = np.arange(0, n + 1, T, dtype=np.int32)
+    empty, zeros = _no_prefix(q, n // T)
+    return prefill_suffix(q, k, v, cu, empty, empty, zeros, scale, rows, heads)
+
+
 def gather_item_prefix(item_tokens, item_ids, tokens_per_item):
     """An item-mode prefix: the listed items' tokens, in list order.
 

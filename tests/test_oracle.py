@@ -327,3 +327,98 @@ def test_planted_mistake_is_caught():
     ref, _ = brute_force(q, k, v, pre, 0.35)
     assert np.abs(wrong[:5] - ref[:5]).max() > 1e-3
     np.testing.assert_allclose(good, ref, atol=1e-12)
+
+
+# ----------------------------------------------- prefix rows and per-item rows
+def _packed_requests(rng, lens, H, D):
+    n = int(sum(lens))
+    q = rng.standard_normal((n, H, D))
+    k = rng.standard_normal((n, H, D))
+    v = rng.standard_normal((n, H, D))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def test_prefix_rows_brute_force_and_suffix_invisible():
+    """Each prefix row matches the explicit-loop definition over its own
+    request's prefix, and equals the prefix rows of the full bipartite
+    attention with a suffix appended (prefix rows never see the suffix)."""
+    rng = np.random.default_rng(21)
+    lens, H, D, scale = [1, 4, 9], 2, 4, 0.37
+    q, k, v, cu = _packed_requests(rng, lens, H, D)
+    out, lse = oracle.prefix_rows(q, k, v, cu, scale)
+    for r, n_p in enumerate(lens):
+        sl = slice(cu[r], cu[r + 1])
+        for h in range(H):
+            bo, bl = brute_force(q[sl, h], k[sl, h], v[sl, h], np.ones(n_p, bool), scale)
+            np.testing.assert_allclose(out[sl, h], bo, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[h, sl], bl, rtol=0, atol=1e-12)
+            # the same request with a random suffix behind its prefix
+            qs, ks, vs, pre = rand_seq(rng, n_p, 3, D)
+            qs[:n_p], ks[:n_p], vs[:n_p] = q[sl, h], k[sl, h], v[sl, h]
+            fo, fl = oracle.bipartite_attention(qs, ks, vs, pre, scale)
+            np.testing.assert_allclose(out[sl, h], fo[:n_p], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[h, sl], fl[:n_p], rtol=0, atol=1e-12)
+
+
+def test_prefix_rows_library_sdpa():
+    """Per request, the prefix rows are unmasked SDPA over that prefix alone."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(22)
+    lens, H, D = [5, 33, 64], 3, 32
+    q, k, v, cu = _packed_requests(rng, lens, H, D)
+    scale = 1.0 / math.sqrt(D)
+    out, _ = oracle.prefix_rows(q, k, v, cu, scale)
+    for r in range(len(lens)):
+        sl = slice(cu[r], cu[r + 1])
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x[sl].transpose(1, 0, 2)))[None]
+        ref = F.scaled_dot_product_attention(t(q), t(k), t(v), scale=scale)[0]
+        np.testing.assert_allclose(out[sl], ref.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def test_item_local_single_token_items():
+    """T = 1: every row sees only itself, so out = v and lse = scale * q.k."""
+    rng = np.random.default_rng(23)
+    q, k, v, _ = _packed_requests(rng, [7], 2, 8)
+    out, lse = oracle.item_local(q, k, v, 1, 0.3)
+    np.testing.assert_allclose(out, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.3 * np.einsum("thd,thd->ht", q, k), rtol=0, atol=1e-14)
+
+
+def test_item_local_equal_keys_give_item_mean():
+    """Equal keys inside an item: each row returns the mean of its item's
+    values, and lse = scale * q.k + ln T."""
+    rng = np.random.default_rng(24)
+    T, n_items, H, D, scale = 4, 3, 2, 8, 0.5
+    q = rng.standard_normal((n_items * T, H, D))
+    v = rng.standard_normal((n_items * T, H, D))
+    kk = rng.standard_normal((n_items, 1, H, D))
+    k = np.repeat(kk, T, axis=1).reshape(n_items * T, H, D)
+    out, lse = oracle.item_local(q, k, v, T, scale)
+    mean = v.reshape(n_items, T, H, D).mean(axis=1)
+    np.testing.assert_allclose(out.reshape(n_items, T, H, D), np.repeat(mean[:, None], T, 1),
+                               rtol=0, atol=1e-14)
+    ref_lse = scale * np.einsum("thd,thd->ht", q, k) + math.log(T)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-13)
+
+
+def test_item_local_brute_force_and_isolation():
+    """Each item matches the explicit-loop definition over its own tokens,
+    and changing every other item leaves it unchanged."""
+    rng = np.random.default_rng(25)
+    T, n_items, H, D, scale = 4, 5, 2, 6, 0.41
+    q, k, v, _ = _packed_requests(rng, [n_items * T], H, D)
+    out, lse = oracle.item_local(q, k, v, T, scale)
+    for i in range(n_items):
+        sl = slice(i * T, (i + 1) * T)
+        for h in range(H):
+            bo, bl = brute_force(q[sl, h], k[sl, h], v[sl, h], np.ones(T, bool), scale)
+            np.testing.assert_allclose(out[sl, h], bo, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[h, sl], bl, rtol=0, atol=1e-12)
+    q2, k2, v2 = (x.copy() for x in (q, k, v))
+    for x in (q2, k2, v2):
+        x[T:] = rng.standard_normal(x[T:].shape)
+    out2, lse2 = oracle.item_local(q2, k2, v2, T, scale)
+    np.testing.assert_array_equal(out2[:T], out[:T])
+    np.testing.assert_array_equal(lse2[:, :T], lse[:, :T])

@@ -100,6 +100,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--workload", choices=("prefill", "prefix-rows", "item-local"),
+                    default="prefill",
+                    help="prefill: bat_attn_prefill on --config (the default line); "
+                         "prefix-rows: bat_attn_prefix_rows over the 8k-history prefixes; "
+                         "item-local: bat_attn_item_local over the 20000-item pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -138,6 +143,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload != "prefill":
+        bench_prefix_workload(args)
+        return
     t0 = time.time()
     wl = W.make_config(args.config)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",
@@ -290,6 +298,136 @@ def run_cpu_baseline(wl, target_s):
             "sample": f"{len(rows)} random (suffix row, head) pairs of {wl.name}, float64, "
                       f"{dt:.1f} s; rate = algorithmic flops of those pairs / time",
             "suffix_tokens_per_s_equiv": round(len(rows) / wl.H / dt, 3)}
+
+
+def _timed_steps(step, steps, warmup, stream):
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return wall_ms, float(per.mean())
+
+
+def bench_prefix_workload(args):
+    """The prefix-building rows: prefix rows over the 8k-history prefixes
+    (16 requests x 8192 tokens, H=16, D=128, bf16; MFMA-bound) or per-item
+    rows over the item pool of the item-prefix configuration (20000 items x 4
+    tokens, H=8, D=64, bf16; HBM-bound).  Seeded N(0, 1) inputs; one JSON line
+    in the same form as the default one."""
+    import numpy as np
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd import workloads as W
+    from prefix_reuse_attention_amd.device import to_device
+
+    rng = np.random.default_rng(2024)
+    stream = torch.cuda.current_stream()
+    if args.workload == "prefix-rows":
+        B, n_p, H, D = 16, 8192, 16, 128
+        n = B * n_p
+        desc = f"prefix rows of the 8k-history prefixes: B={B} x {n_p} tokens, H={H}, D={D}, bf16"
+        flops = 4.0 * B * n_p * n_p * D * H
+    else:
+        n_items, T, H, D = 20000, W.ITEM_TOKENS, 8, 64
+        n = n_items * T
+        desc = f"per-item rows of the item pool: {n_items} items x {T} tokens, H={H}, D={D}, bf16"
+        flops = 4.0 * n_items * T * T * D * H
+    q, k, v = (W._normal(rng, (n, H, D), "bf16") for _ in range(3))
+    dq, dk, dv = (to_device(a, "bf16") for a in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(dq)
+    lse = torch.empty((H, n), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    if args.workload == "prefix-rows":
+        cu = torch.arange(0, n + 1, n_p, dtype=torch.int32, device="cuda")
+        ws = torch.empty(api.workspace_size(B, H, D, api.BAT_BF16, n, n_p, 0), dtype=torch.uint8,
+                         device="cuda")
+        step = lambda: api.attn_prefix_rows(dq, dk, dv, cu, softmax_scale=scale, max_prefix_len=n_p,
+                                            out=out, lse=lse, workspace=ws)
+    else:
+        step = lambda: api.attn_item_local(dq, dk, dv, T, softmax_scale=scale, out=out, lse=lse)
+    steps = args.steps if args.workload == "item-local" else max(1, min(args.steps, 20))
+    warmup = args.warmup if args.workload == "item-local" else max(1, min(args.warmup, 5))
+    wall_ms, kernel_ms = _timed_steps(step, steps, warmup, stream)
+    alg_bytes = 4.0 * n * H * D * 2 + 4.0 * n * H  # q, k, v read, out written; lse
+    line = {"workload": args.workload, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(wall_ms, 5), "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) activations)",
+            "config": {"workload": desc}, "alg_flops_per_step": flops,
+            "alg_bytes_per_step": alg_bytes}
+    if args.workload == "prefix-rows":
+        line.update({"metric": "prefix-row attention TFLOP/s, 1 GPU",
+                     "value": round(flops / (wall_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                     "higher_is_better": True,
+                     "roofline": {"bound": "mfma", "achieved": round(flops / (kernel_ms * 1e-3) / 1e12, 3),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(flops / (kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": None, "kernel_ms_mean": round(kernel_ms, 5)}})
+    else:
+        gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+        line.update({"metric": "per-item row attention GB/s, 1 GPU",
+                     "value": round(alg_bytes / (wall_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                     "higher_is_better": True,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                  "traffic": None, "kernel_ms_mean": round(kernel_ms, 5)}})
+    print(f"[bench] {args.workload}: {wall_ms:.4f} ms/step (events {kernel_ms:.4f} ms)",
+          file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _prefix_cpu_baseline(args.workload, rng, H, D, scale,
+                                                    n_p if args.workload == "prefix-rows" else T,
+                                                    args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def _prefix_cpu_baseline(workload, rng, H, D, scale, span, target_s):
+    """The oracle on a bounded sample of the same workload: whole requests of
+    `span` prefix tokens (prefix rows, on sampled rows) or whole items."""
+    import numpy as np
+    import oracle
+    from prefix_reuse_attention_amd import workloads as W
+    if workload == "prefix-rows":
+        q, k, v = (W._normal(rng, (span, H, D), "bf16") for _ in range(3))
+        cu = np.array([0, span], np.int32)
+        n = 64
+        while True:
+            rows = rng.integers(0, span, n).astype(np.int32)
+            heads = rng.integers(0, H, n).astype(np.int32)
+            t = time.perf_counter()
+            oracle.prefix_rows(q, k, v, cu, scale, rows=rows, heads=heads)
+            dt = time.perf_counter() - t
+            if dt >= target_s / 4:
+                break
+            n = int(max(2 * n, n * (target_s / 2) / max(dt, 1e-3)))
+        fl = 4.0 * len(rows) * span * D
+        return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": f"{len(rows)} random (prefix row, head) pairs of one {span}-token prefix, "
+                          f"float64, {dt:.1f} s"}
+    n_items = 1024
+    while True:
+        q, k, v = (W._normal(rng, (n_items * span, H, D), "bf16") for _ in range(3))
+        t = time.perf_counter()
+        oracle.item_local(q, k, v, span, scale)
+        dt = time.perf_counter() - t
+        if dt >= target_s / 4 or n_items >= 20000:
+            break
+        n_items = int(min(20000, max(2 * n_items, n_items * (target_s / 2) / max(dt, 1e-3))))
+    by = 4.0 * n_items * span * H * D * 2 + 4.0 * n_items * span * H
+    return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_items} items x {span} tokens, all heads, float64, {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -18,8 +18,9 @@
  * of P and U:
  *     S_ij = softmax_scale * <q_i, k_j>
  *     lse_i = ln sum_j exp(S_ij),   out_i = sum_j exp(S_ij - lse_i) v_j.
- * (Prefix rows would see P only; their outputs are what was cached and are
- * not recomputed here.)
+ * A prefix row sees P only (bat_attn_prefix_rows); in an item pool, a
+ * cached item's own tokens can instead see only their item
+ * (bat_attn_item_local).  These build the prefix for the next layer.
  *
  * Conventions for every entry point
  *   - Ownership: the caller owns every buffer.  The library allocates no
@@ -161,6 +162,66 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                             int32_t max_prefix_len, void *out, float *lse,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * bat_attn_prefix_rows -- attention of the prefix rows over their prefix.
+ *
+ * The prefix rows of the bipartite mask: a prefix token sees every token of
+ * its own request's prefix and nothing of the suffix (the UG-Separation
+ * page's abstract: the tokens kept purely user-side are the ones whose
+ * key/value cache can be reused; with no positions or causal mask on the Bat
+ * page, the prefix attends bidirectionally within itself).  This is how the
+ * cached keys/values of the next layer are produced from this layer's
+ * prefix.  For an item prefix it is the prefix-wide form (every listed item
+ * sees all of them); see bat_attn_item_local for items that see only
+ * themselves.
+ *
+ *   q, k, v         device, packed prefix [total_prefix, H, D], dtype dt
+ *   cu_prefix_lens  device int32 [B+1]: request r owns rows
+ *                   cu_prefix_lens[r] .. cu_prefix_lens[r+1]
+ *   softmax_scale   multiplies q.k
+ *   total_prefix    host copy of cu_prefix_lens[B]; 0 is a no-op
+ *   max_prefix_len  host upper bound over requests (> 0 unless total is 0)
+ *   out             device [total_prefix, H, D], dtype dt
+ *   lse             device float32 [H, total_prefix] (natural log), or NULL
+ *   workspace       device, >= bat_attn_workspace_size(B, H, D, dt,
+ *                   total_prefix, max_prefix_len, 0) bytes
+ * Same kernels, dtypes and head dims as bat_attn_prefill.
+ */
+bat_status bat_attn_prefix_rows(const void *q, const void *k, const void *v,
+                                const int32_t *cu_prefix_lens, int32_t B,
+                                int32_t H, int32_t D, bat_dtype dt,
+                                float softmax_scale, int32_t total_prefix,
+                                int32_t max_prefix_len, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * bat_attn_item_local -- attention of each cached item's tokens within that
+ * item only (the per-item, block-diagonal variant of the prefix rows).
+ *
+ * The Bat page's item-as-prefix mode reuses popular items' key/value blocks
+ * from a shared pool in whatever combination a request lists them
+ * (sections "This paper's idea" and "Why it works"); an item's cached
+ * keys/values beyond the first layer can only be shared that way when its
+ * tokens attended to nothing but their own item.  Item i owns rows
+ * i*T .. i*T+T-1 of the packed inputs; each such row sees exactly those T
+ * keys: S_ab = softmax_scale * <q_a, k_b>, lse_a = ln sum_b exp(S_ab),
+ * out_a = sum_b exp(S_ab - lse_a) v_b.
+ *
+ *   q, k, v          device, packed [n_items * T, H, D], dtype dt
+ *   n_items          items; n_items * T rows and n_items * H (item, head)
+ *                    pairs must stay below 2^31 (else BAT_ERR_INVALID_ARG)
+ *   tokens_per_item  T, one of 1, 2, 4, 8 (else BAT_ERR_UNSUPPORTED)
+ *   out              device [n_items * T, H, D], dtype dt
+ *   lse              device float32 [H, n_items * T] (natural log), or NULL
+ * Dtypes and head dims as bat_attn_prefill.  Needs no workspace.
+ */
+bat_status bat_attn_item_local(const void *q, const void *k, const void *v,
+                               int32_t n_items, int32_t tokens_per_item,
+                               int32_t H, int32_t D, bat_dtype dt,
+                               float softmax_scale, void *out, float *lse,
+                               void *stream);
 
 /*
  * bat_lse_merge -- combine n_parts attention partials over disjoint key sets

@@ -17,7 +17,8 @@ BAT_OK, BAT_ERR_INVALID_ARG, BAT_ERR_UNSUPPORTED, BAT_ERR_BLOCK_TABLE, BAT_ERR_W
 BAT_F32, BAT_BF16 = 0, 1
 BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 
-EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill", "bat_lse_merge",
+EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill",
+            "bat_attn_prefix_rows", "bat_attn_item_local", "bat_lse_merge",
             "bat_status_string", "bat_version")
 
 _lib = None
@@ -52,6 +53,11 @@ def load():
     lib.bat_attn_prefill.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I, I,
                                      P, P, P, ctypes.c_size_t, P]
     lib.bat_attn_prefill.restype = I
+    lib.bat_attn_prefix_rows.argtypes = [P, P, P, P, I, I, I, I, F, I, I, P, P, P,
+                                         ctypes.c_size_t, P]
+    lib.bat_attn_prefix_rows.restype = I
+    lib.bat_attn_item_local.argtypes = [P, P, P, I, I, I, I, I, F, P, P, P]
+    lib.bat_attn_item_local.restype = I
     lib.bat_lse_merge.argtypes = [P, P, I, I, I, I, I, P, P, P]
     lib.bat_lse_merge.restype = I
     lib.bat_status_string.argtypes = [I]
@@ -201,6 +207,67 @@ def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
         B, H, D, dt, float(softmax_scale), total, int(max_suffix_len), int(max_prefix_len),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "bat_attn_prefill")
+    return out, lse
+
+
+def attn_prefix_rows(q, k, v, cu_prefix_lens, softmax_scale=None, max_prefix_len=None,
+                     out=None, lse=None, workspace=None, want_lse=False):
+    """Prefix rows over their own request's prefix (packed [total_prefix, H, D]).
+
+    Returns (out, lse); lse is [H, total_prefix] float32 or None.
+    """
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(cu_prefix_lens, "cu_prefix_lens", torch.int32)
+    total, H, D = q.shape
+    B = cu_prefix_lens.shape[0] - 1
+    if max_prefix_len is None:
+        max_prefix_len = int((cu_prefix_lens[1:] - cu_prefix_lens[:-1]).max().item()) if B else 0
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    ws_bytes = workspace_size(B, H, D, dt, total, max_prefix_len, 0)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = load().bat_attn_prefix_rows(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_prefix_lens), B, H, D, dt, float(softmax_scale),
+        total, int(max_prefix_len), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+        _stream())
+    _check(st, "bat_attn_prefix_rows")
+    return out, lse
+
+
+def attn_item_local(q, k, v, tokens_per_item, softmax_scale=None, out=None, lse=None,
+                    want_lse=False):
+    """Each item's tokens attend within the item (packed [n_items * T, H, D])."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    total, H, D = q.shape
+    T = int(tokens_per_item)
+    if T <= 0 or total % T:
+        raise ValueError("rows must be a whole number of items")
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    st = load().bat_attn_item_local(_ptr(q), _ptr(k), _ptr(v), total // T, T, H, D,
+                                    _dtype_code(q), float(softmax_scale), _ptr(out), _ptr(lse),
+                                    _stream())
+    _check(st, "bat_attn_item_local")
     return out, lse
 
 

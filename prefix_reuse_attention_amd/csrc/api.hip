@@ -20,6 +20,9 @@ hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t str
 hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
                             int H, int D, bool bf16, void *out, float *lse, hipStream_t stream);
+hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_t n_items,
+                             int32_t T, int32_t H, int32_t D, bool bf16, float scale_log2,
+                             void *out, float *lse, hipStream_t stream);
 int bf16_rows_per_item(int W);
 int bf16_keys_per_tile(int D);
 int f32_rows_per_item();
@@ -196,24 +199,21 @@ size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
   return pl.total;
 }
 
-bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
-                            const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
-                            const uint8_t *prefix_mode, const int32_t *block_table,
-                            int32_t bt_stride, const bat_kv_pool *user_pool,
-                            const bat_kv_pool *item_pool, int32_t B, int32_t H, int32_t D,
-                            bat_dtype dt, float softmax_scale, int32_t total_suffix,
-                            int32_t max_suffix_len, int32_t max_prefix_len, void *out,
-                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
-  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
-      bt_stride < 0)
-    return BAT_ERR_INVALID_ARG;
-  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
-  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
-  if (total_suffix == 0) return BAT_OK;  // nothing to write
-  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
-  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
-    return BAT_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace bat {
+namespace {
+
+// The attention call behind bat_attn_prefill and bat_attn_prefix_rows: rows
+// cu[r] .. cu[r+1] of q attend to request r's prefix (none when prefix_lens
+// is null) and to the same rows of k/v.  Arguments are checked by the callers.
+bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t *cu_suffix_lens,
+                     const int32_t *prefix_lens, const uint8_t *prefix_mode,
+                     const int32_t *block_table, int32_t bt_stride, const bat_kv_pool *user_pool,
+                     const bat_kv_pool *item_pool, int32_t B, int32_t H, int32_t D, bat_dtype dt,
+                     float softmax_scale, int32_t total_suffix, int32_t max_suffix_len,
+                     int32_t max_prefix_len, void *out, float *lse, void *workspace,
+                     size_t workspace_bytes, void *stream) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -273,6 +273,73 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
       return BAT_ERR_HIP;
     if (h_err) return BAT_ERR_BLOCK_TABLE;
   }
+  return BAT_OK;
+}
+
+}  // namespace
+}  // namespace bat
+
+extern "C" {
+
+bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
+                            const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                            const uint8_t *prefix_mode, const int32_t *block_table,
+                            int32_t bt_stride, const bat_kv_pool *user_pool,
+                            const bat_kv_pool *item_pool, int32_t B, int32_t H, int32_t D,
+                            bat_dtype dt, float softmax_scale, int32_t total_suffix,
+                            int32_t max_suffix_len, int32_t max_prefix_len, void *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
+      bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  return attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table, bt_stride,
+                   user_pool, item_pool, B, H, D, dt, softmax_scale, total_suffix, max_suffix_len,
+                   max_prefix_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+bat_status bat_attn_prefix_rows(const void *q, const void *k, const void *v,
+                                const int32_t *cu_prefix_lens, int32_t B, int32_t H, int32_t D,
+                                bat_dtype dt, float softmax_scale, int32_t total_prefix,
+                                int32_t max_prefix_len, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || total_prefix < 0 || max_prefix_len < 0) return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_prefix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_prefix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_prefix_lens || !out) return BAT_ERR_INVALID_ARG;
+  // a prefix row sees its request's prefix only: the prefix is the row
+  // group itself, with no cached keys before it
+  return attn_rows(q, k, v, cu_prefix_lens, nullptr, nullptr, nullptr, 0, nullptr, nullptr, B,
+                   H, D, dt, softmax_scale, total_prefix, max_prefix_len, 0, out, lse, workspace,
+                   workspace_bytes, stream);
+}
+
+bat_status bat_attn_item_local(const void *q, const void *k, const void *v, int32_t n_items,
+                               int32_t tokens_per_item, int32_t H, int32_t D, bat_dtype dt,
+                               float softmax_scale, void *out, float *lse, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (n_items < 0 || H <= 0) return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  const int T = tokens_per_item;
+  if (!(T == 1 || T == 2 || T == 4 || T == 8)) return BAT_ERR_UNSUPPORTED;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if ((int64_t)n_items * T > 0x7fffffff || (int64_t)n_items * H > 0x7fff0000)
+    return BAT_ERR_INVALID_ARG;
+  if (n_items == 0) return BAT_OK;
+  if (!q || !k || !v || !out) return BAT_ERR_INVALID_ARG;
+  const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  if (launch_item_local(q, k, v, n_items, T, H, D, dt == BAT_BF16, scale_log2, out, lse,
+                        (hipStream_t)stream) != hipSuccess)
+    return BAT_ERR_HIP;
   return BAT_OK;
 }
 

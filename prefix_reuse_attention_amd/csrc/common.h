@@ -43,8 +43,8 @@ struct ReqMeta {
 struct AttnParams {
   const void *q, *k, *v;          // packed suffix [total_s, H, D]
   const int32_t *cu_s;            // [B+1]
-  const int32_t *prefix_lens;     // [B]
-  const uint8_t *prefix_mode;     // [B]
+  const int32_t *prefix_lens;     // [B], or null: no prefixes
+  const uint8_t *prefix_mode;     // [B], or null
   const int32_t *block_table;     // [B, bt_stride]
   const void *pool_k[2];          // user, item
   const void *pool_v[2];
@@ -76,8 +76,9 @@ __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) 
   ItemRange x;
   x.q0 = p.cu_s[it.r];
   x.n_s = p.cu_s[it.r + 1] - x.q0;
-  x.n_p = min(max(p.prefix_lens[it.r], 0), p.max_prefix);
-  x.mode = p.prefix_mode[it.r] ? 1 : 0;
+  // no prefix arrays (prefix-row attention): every request has an empty prefix
+  x.n_p = p.prefix_lens ? min(max(p.prefix_lens[it.r], 0), p.max_prefix) : 0;
+  x.mode = p.prefix_mode && p.prefix_mode[it.r] ? 1 : 0;
   const ReqMeta m = p.meta[it.r];
   x.n_chunks = m.n_chunks;
   x.part_off = m.part_off;

@@ -1,0 +1,171 @@
+// Attention inside each cached item of an item pool (the per-item
+// block-diagonal prefix rows).
+//
+// On the Bat page, a request whose prefix is a set of popular items reuses
+// those items' key/value blocks from a shared pool (sections "This paper's
+// idea" and "Why it works"); an item's cached K/V can only be reused in any
+// combination of items if the item's own tokens never saw the others, so the
+// prefix rows of an item prefix attend within their own item.  Item i owns
+// tokens i*T .. i*T+T-1 of the packed [n_items*T, H, D] inputs; each of its
+// rows sees exactly those T keys (no positions, no causal mask):
+//     S_ab = scale * <q_a, k_b>,  lse_a = ln sum_b exp(S_ab),
+//     out_a = sum_b exp(S_ab - lse_a) v_b          (a, b within the item).
+//
+// A group of G = D / (elements per 16 bytes) lanes serves one (item, head):
+// each lane loads its 16-byte slice of the item's T query, key and value
+// rows (coalesced: a group reads whole rows), forms the T*T partial dot
+// products of its slice, and the group sums them with lane shuffles.  Every
+// lane then holds the item's T*T scores, takes the softmax in fp32 and writes
+// its slice of the T output rows.  T*T and G are small, so the kernel is
+// bound by the 3*T reads and T writes of D elements per (item, head).
+#include "common.h"
+
+namespace bat {
+
+// 16 bytes of a bf16 or fp32 row as floats.
+template <bool BF16>
+struct Slice {
+  static constexpr int N = BF16 ? 8 : 4;
+  u32x4 w;
+  __device__ __forceinline__ float at(int e) const {
+    if constexpr (BF16) {
+      const uint32_t x = w[e >> 1];
+      return __builtin_bit_cast(float, (e & 1) ? (x & 0xffff0000u) : (x << 16));
+    } else {
+      // through a scalar: a bit_cast of the element expression itself would
+      // read the vector's first element
+      const uint32_t x = w[e];
+      return __builtin_bit_cast(float, x);
+    }
+  }
+};
+
+template <int D, int T, bool BF16>
+__global__ __launch_bounds__(256) void item_local_kernel(const void *__restrict__ q,
+                                                         const void *__restrict__ k,
+                                                         const void *__restrict__ v,
+                                                         int32_t n_items, int32_t H,
+                                                         float scale_log2, void *__restrict__ out,
+                                                         float *__restrict__ lse) {
+  using S = Slice<BF16>;
+  constexpr int EB = BF16 ? 2 : 4;  // bytes per element
+  constexpr int G = D / S::N;       // lanes per (item, head)
+  constexpr int GPW = kWave / G;    // groups per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  // (item, head) pairs number below 2^31 (checked by the caller)
+  const int grp = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave)) * GPW + lane / G;
+  // a group is whole lanes of one wave: either all of its lanes leave here
+  // or none, so the shuffles below stay inside live groups
+  if (grp >= n_items * H) return;
+  const int c = lane % G;
+  const int item = grp / H, head = grp - item * H;
+  const int64_t row0 = (int64_t)item * T;
+
+  S qs[T], ks[T], vs[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t off = (((row0 + t) * H + head) * D + (int64_t)c * S::N) * EB;
+    qs[t].w = *(const u32x4 *)((const uint8_t *)q + off);
+    ks[t].w = *(const u32x4 *)((const uint8_t *)k + off);
+    vs[t].w = *(const u32x4 *)((const uint8_t *)v + off);
+  }
+
+  // this lane's share of every dot product, then the group's sum
+  float s[T][T];
+#pragma unroll
+  for (int a = 0; a < T; ++a)
+#pragma unroll
+    for (int b = 0; b < T; ++b) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::N; ++e) acc = __builtin_fmaf(qs[a].at(e), ks[b].at(e), acc);
+      s[a][b] = acc;
+    }
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1)
+#pragma unroll
+    for (int a = 0; a < T; ++a)
+#pragma unroll
+      for (int b = 0; b < T; ++b) s[a][b] += __shfl_xor(s[a][b], m, G);
+
+  // softmax per row in the log2 domain, then this lane's slice of the output
+  const int64_t total = (int64_t)n_items * T;
+#pragma unroll
+  for (int a = 0; a < T; ++a) {
+    float mx = s[a][0];
+#pragma unroll
+    for (int b = 1; b < T; ++b) mx = fmaxf(mx, s[a][b]);
+    const float m2 = mx * scale_log2;
+    float p[T], l = 0.f;
+#pragma unroll
+    for (int b = 0; b < T; ++b) {
+      p[b] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[a][b], scale_log2, -m2));
+      l += p[b];
+    }
+    const float inv = 1.0f / l;
+    float o[S::N];
+#pragma unroll
+    for (int e = 0; e < S::N; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int b = 0; b < T; ++b) acc = __builtin_fmaf(p[b], vs[b].at(e), acc);
+      o[e] = acc * inv;
+    }
+    const int64_t off = (((row0 + a) * H + head) * D + (int64_t)c * S::N) * EB;
+    if constexpr (BF16) {
+      typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+      typedef float f32x8 __attribute__((ext_vector_type(8)));
+      const f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+      const bf16x8_t h = __builtin_convertvector(f, bf16x8_t);  // round to nearest even
+      *(u32x4 *)((uint8_t *)out + off) = __builtin_bit_cast(u32x4, h);
+    } else {
+      const f32x4 f = {o[0], o[1], o[2], o[3]};
+      *(f32x4 *)((uint8_t *)out + off) = f;
+    }
+    if (lse && c == 0) lse[(int64_t)head * total + row0 + a] = (m2 + __log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+template <int D, int T, bool BF16>
+hipError_t launch_item_local_t(const void *q, const void *k, const void *v, int32_t n_items,
+                               int32_t H, float scale_log2, void *out, float *lse,
+                               hipStream_t stream) {
+  constexpr int G = D / (BF16 ? 8 : 4);
+  constexpr int groups_per_block = 4 * (kWave / G);  // four waves
+  const int64_t groups = (int64_t)n_items * H;
+  if (groups > 0x7fffffff - groups_per_block) return hipErrorInvalidValue;
+  const int64_t blocks = (groups + groups_per_block - 1) / groups_per_block;
+  hipLaunchKernelGGL((item_local_kernel<D, T, BF16>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, q, k, v, n_items, H, scale_log2, out, lse);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_item_local_d(const void *q, const void *k, const void *v, int32_t n_items,
+                               int32_t T, int32_t H, float scale_log2, void *out, float *lse,
+                               hipStream_t stream) {
+  switch (T) {
+    case 1: return launch_item_local_t<D, 1, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
+    case 2: return launch_item_local_t<D, 2, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
+    case 4: return launch_item_local_t<D, 4, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
+    case 8: return launch_item_local_t<D, 8, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Tokens per item T in {1, 2, 4, 8}; (dtype, D) as the attention kernels.
+hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_t n_items,
+                             int32_t T, int32_t H, int32_t D, bool bf16, float scale_log2,
+                             void *out, float *lse, hipStream_t stream) {
+  if (bf16) {
+    if (D == 64) return launch_item_local_d<64, true>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+    if (D == 128) return launch_item_local_d<128, true>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+  } else {
+    if (D == 32) return launch_item_local_d<32, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+    if (D == 64) return launch_item_local_d<64, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+    if (D == 128) return launch_item_local_d<128, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bat

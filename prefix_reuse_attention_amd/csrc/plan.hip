@@ -89,7 +89,7 @@ __device__ __forceinline__ void plan_body(
     int32_t part[1] = {0}, tot[1];
     for (int r = k0; r < k1; ++r) {
       const int n_s = cu_s[r + 1] - cu_s[r];
-      const int n_p = min(max(prefix_lens[r], 0), max_p);
+      const int n_p = prefix_lens ? min(max(prefix_lens[r], 0), max_p) : 0;
       int nc = 1;
       if (chunk_len > 0 && n_p > chunk_len) nc = (n_p + chunk_len - 1) / chunk_len;
       req_nc[r] = nc;

@@ -137,6 +137,63 @@ def test_workspace_size(lib):
     assert f(1, 2, 128, api.BAT_BF16, 64, 64, 16384) > f(1, 2, 128, api.BAT_BF16, 64, 64, 1024)
 
 
+def prefix_rows(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=2, H=8, D=128, dt=api.BAT_BF16, scale=0.088,
+             total=1024, max_p=512, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    if a["ws_bytes"] == "exact-1":
+        a["ws_bytes"] = lib.bat_attn_workspace_size(a["B"], a["H"], a["D"], a["dt"], a["total"],
+                                                    a["max_p"], 0) - 1
+    return lib.bat_attn_prefix_rows(a["q"], a["k"], a["v"], a["cu"], a["B"], a["H"], a["D"],
+                                    a["dt"], a["scale"], a["total"], a["max_p"], a["out"],
+                                    a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BAT_ERR_INVALID_ARG),
+    (dict(k=None), api.BAT_ERR_INVALID_ARG),
+    (dict(out=None), api.BAT_ERR_INVALID_ARG),
+    (dict(cu=None), api.BAT_ERR_INVALID_ARG),
+    (dict(scale=0.0), api.BAT_ERR_INVALID_ARG),
+    (dict(H=0), api.BAT_ERR_INVALID_ARG),
+    (dict(B=-1), api.BAT_ERR_INVALID_ARG),
+    (dict(max_p=0), api.BAT_ERR_INVALID_ARG),
+    (dict(D=32), api.BAT_ERR_UNSUPPORTED),
+    (dict(dt=7), api.BAT_ERR_INVALID_ARG),
+    (dict(ws=None), api.BAT_ERR_WORKSPACE),
+    (dict(ws_bytes="exact-1"), api.BAT_ERR_WORKSPACE),
+    (dict(total=0), api.BAT_OK),                       # no prefix rows: nothing to write
+])
+def test_prefix_rows_argument_errors(lib, over, status):
+    assert prefix_rows(lib, **over) == status
+
+
+def item_local(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, n=100, T=4, H=8, D=64, dt=api.BAT_BF16, scale=0.125,
+             out=FAKE, lse=None, stream=None)
+    a.update(over)
+    return lib.bat_attn_item_local(a["q"], a["k"], a["v"], a["n"], a["T"], a["H"], a["D"],
+                                   a["dt"], a["scale"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BAT_ERR_INVALID_ARG),
+    (dict(v=None), api.BAT_ERR_INVALID_ARG),
+    (dict(out=None), api.BAT_ERR_INVALID_ARG),
+    (dict(n=-1), api.BAT_ERR_INVALID_ARG),
+    (dict(H=0), api.BAT_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), api.BAT_ERR_INVALID_ARG),
+    (dict(T=3), api.BAT_ERR_UNSUPPORTED),              # T in {1, 2, 4, 8}
+    (dict(T=16), api.BAT_ERR_UNSUPPORTED),
+    (dict(D=32), api.BAT_ERR_UNSUPPORTED),
+    (dict(dt=5), api.BAT_ERR_INVALID_ARG),
+    (dict(n=1 << 29, T=8), api.BAT_ERR_INVALID_ARG),   # rows beyond int32
+    (dict(n=0), api.BAT_OK),
+])
+def test_item_local_argument_errors(lib, over, status):
+    assert item_local(lib, **over) == status
+
+
 def test_lse_merge_argument_errors(lib):
     m = lib.bat_lse_merge
     assert m(FAKE, FAKE, 0, 10, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG

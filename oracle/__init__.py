@@ -192,6 +192,51 @@ def item_local(q, k, v, tokens_per_item, scale, rows=None, heads=None):
     return prefill_suffix(q, k, v, cu, empty, empty, zeros, scale, rows, heads)
 
 
+def _widen(x):
+    """float64 values of a float32 or bf16-bits (uint16) array, exactly."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, tokens_per_candidate, scale,
+                     rows=None, heads=None):
+    """Candidate-isolated suffix rows, float64, written out plainly.
+
+    Request r's suffix rows cu_s[r]:cu_s[r+1] form candidates of T =
+    tokens_per_candidate consecutive tokens; a row sees every prefix token of
+    its request (rows cu_p[r]:cu_p[r+1] of k_p/v_p) and the T tokens of its own
+    candidate, nothing else.  Per visible set: max, exp-sum, normalised sum.
+    Returns (out, lse) shaped as prefill_suffix's.
+    """
+    cu_s = np.asarray(cu_s, np.int64)
+    cu_p = np.asarray(cu_p, np.int64)
+    T = int(tokens_per_candidate)
+    total_s, H, D = np.asarray(q).shape
+    if rows is None:
+        sel_r = np.repeat(np.arange(total_s), H)
+        sel_h = np.tile(np.arange(H), total_s)
+    else:
+        sel_r, sel_h = np.asarray(rows, np.int64), np.asarray(heads, np.int64)
+    out = np.zeros((len(sel_r), D))
+    lse = np.zeros(len(sel_r))
+    for n, (i, h) in enumerate(zip(sel_r, sel_h)):
+        r = int(np.searchsorted(cu_s, i, side="right") - 1)
+        c0 = cu_s[r] + ((i - cu_s[r]) // T) * T
+        keys = np.concatenate([_widen(k_p[cu_p[r]:cu_p[r + 1], h]), _widen(k_s[c0:c0 + T, h])])
+        vals = np.concatenate([_widen(v_p[cu_p[r]:cu_p[r + 1], h]), _widen(v_s[c0:c0 + T, h])])
+        sc = scale * (keys @ _widen(q[i, h]))
+        m = sc.max()
+        w = np.exp(sc - m)
+        z = w.sum()
+        lse[n] = m + math.log(z)
+        out[n] = (w / z) @ vals
+    if rows is None:
+        return out.reshape(total_s, H, D), lse.reshape(total_s, H).T.copy()
+    return out, lse
+
+
 def gather_item_prefix(item_tokens, item_ids, tokens_per_item):
     """An item-mode prefix: the listed items' tokens, in list order.
 

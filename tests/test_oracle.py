@@ -422,3 +422,95 @@ def test_item_local_brute_force_and_isolation():
     out2, lse2 = oracle.item_local(q2, k2, v2, T, scale)
     np.testing.assert_array_equal(out2[:T], out[:T])
     np.testing.assert_array_equal(lse2[:, :T], lse[:, :T])
+
+
+# ------------------------------------------------ candidate-isolated suffix rows
+def _iso_case(rng, lens_p, lens_s, H, D):
+    k_p = rng.standard_normal((sum(lens_p), H, D))
+    v_p = rng.standard_normal((sum(lens_p), H, D))
+    q = rng.standard_normal((sum(lens_s), H, D))
+    k_s = rng.standard_normal((sum(lens_s), H, D))
+    v_s = rng.standard_normal((sum(lens_s), H, D))
+    cu_p = np.concatenate([[0], np.cumsum(lens_p)]).astype(np.int32)
+    cu_s = np.concatenate([[0], np.cumsum(lens_s)]).astype(np.int32)
+    return q, k_s, v_s, cu_s, k_p, v_p, cu_p
+
+
+def test_isolated_brute_force():
+    """Explicit visible sets: the request's prefix plus the row's own
+    candidate of T tokens."""
+    rng = np.random.default_rng(31)
+    T, H, D, scale = 2, 2, 3, 0.45
+    lens_p, lens_s = [3, 0, 5], [4, 2, 6]
+    q, k_s, v_s, cu_s, k_p, v_p, cu_p = _iso_case(rng, lens_p, lens_s, H, D)
+    out, lse = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, T, scale)
+    for r in range(3):
+        for i in range(cu_s[r], cu_s[r + 1]):
+            c0 = cu_s[r] + ((i - cu_s[r]) // T) * T
+            for h in range(H):
+                vis = [("p", j) for j in range(cu_p[r], cu_p[r + 1])] + \
+                      [("s", j) for j in range(c0, c0 + T)]
+                kk = lambda t, j: (k_p if t == "p" else k_s)[j, h]
+                vv = lambda t, j: (v_p if t == "p" else v_s)[j, h]
+                sc = [scale * sum(float(q[i, h, d]) * float(kk(t, j)[d]) for d in range(D))
+                      for t, j in vis]
+                z = sum(math.exp(x) for x in sc)
+                ref = sum(math.exp(x) / z * vv(t, j) for x, (t, j) in zip(sc, vis))
+                np.testing.assert_allclose(out[i, h], ref, rtol=0, atol=1e-12)
+                assert abs(lse[h, i] - math.log(z)) <= 1e-12
+
+
+def test_isolated_one_candidate_is_the_plain_prefill():
+    """T = n_s (one candidate per request): the ordinary suffix prefill."""
+    rng = np.random.default_rng(32)
+    lens_p, lens_s, H, D = [7, 0, 12], [4, 4, 4], 2, 8
+    q, k_s, v_s, cu_s, k_p, v_p, cu_p = _iso_case(rng, lens_p, lens_s, H, D)
+    out, lse = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, 4, 0.3)
+    ref, ref_lse = oracle.prefill_suffix(q, k_s, v_s, cu_s, k_p, v_p, cu_p, 0.3)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_isolated_is_merge_of_prefix_and_candidate_parts():
+    """Prefix part (rows over the prefix alone, masked attention) merged with
+    the candidate part (per-item rows) gives the isolated rows; with no
+    prefix the isolated rows are the per-item rows themselves."""
+    rng = np.random.default_rng(33)
+    T, H, D, scale = 4, 2, 8, 0.35
+    lens_p, lens_s = [9, 0], [8, 12]
+    q, k_s, v_s, cu_s, k_p, v_p, cu_p = _iso_case(rng, lens_p, lens_s, H, D)
+    out, lse = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, T, scale)
+    cand, cand_lse = oracle.item_local(q, k_s, v_s, T, scale)
+    # request 0: prefix part by masked attention of its suffix rows over its prefix
+    sl = slice(cu_s[0], cu_s[1])
+    for h in range(H):
+        po, pl = oracle.attention_masked(q[sl, h], k_p[:9, h], v_p[:9, h],
+                                         np.ones((8, 9), bool), scale)
+        mo, ml = oracle.lse_merge([(po, pl), (cand[sl, h], cand_lse[h, sl])])
+        np.testing.assert_allclose(out[sl, h], mo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h, sl], ml, rtol=0, atol=1e-12)
+    # request 1: no prefix
+    sl = slice(cu_s[1], cu_s[2])
+    np.testing.assert_allclose(out[sl], cand[sl], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, sl], cand_lse[:, sl], rtol=0, atol=1e-12)
+
+
+def test_isolated_single_token_candidates_without_prefix():
+    """T = 1 and no prefix: each row sees only itself (out = v)."""
+    rng = np.random.default_rng(34)
+    q, k_s, v_s, cu_s, k_p, v_p, cu_p = _iso_case(rng, [0, 0], [3, 5], 2, 4)
+    out, lse = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, 1, 0.7)
+    np.testing.assert_allclose(out, v_s, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.7 * np.einsum("thd,thd->ht", q, k_s), rtol=0, atol=1e-14)
+
+
+def test_isolated_selected_rows_match_full():
+    rng = np.random.default_rng(35)
+    q, k_s, v_s, cu_s, k_p, v_p, cu_p = _iso_case(rng, [5, 3], [4, 8], 3, 4)
+    out, lse = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, 2, 0.5)
+    rows = np.array([0, 3, 4, 11], np.int32)
+    heads = np.array([2, 0, 1, 2], np.int32)
+    so, sl = oracle.prefill_isolated(q, k_s, v_s, cu_s, k_p, v_p, cu_p, 2, 0.5, rows=rows,
+                                     heads=heads)
+    np.testing.assert_array_equal(so, out[rows, heads])
+    np.testing.assert_array_equal(sl, lse[heads, rows])

@@ -100,11 +100,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--workload", choices=("prefill", "prefix-rows", "item-local"),
+    ap.add_argument("--workload", choices=("prefill", "isolated", "prefix-rows", "item-local"),
                     default="prefill",
                     help="prefill: bat_attn_prefill on --config (the default line); "
-                         "prefix-rows: bat_attn_prefix_rows over the 8k-history prefixes; "
-                         "item-local: bat_attn_item_local over the 20000-item pool")
+                         "isolated: bat_attn_prefill_isolated on --config with single-token "
+                         "candidates; prefix-rows: bat_attn_prefix_rows over the 8k-history "
+                         "prefixes; item-local: bat_attn_item_local over the 20000-item pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -143,9 +144,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if args.workload != "prefill":
+    if args.workload in ("prefix-rows", "item-local"):
         bench_prefix_workload(args)
         return
+    isolated = args.workload == "isolated"
     t0 = time.time()
     wl = W.make_config(args.config)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",
@@ -172,8 +174,19 @@ def main():
     out = torch.empty_like(dw.q)
     lse = torch.empty((wl.H, wl.total_s), dtype=torch.float32, device="cuda")
 
-    def step():
-        dw.run(out=out, lse=lse, workspace=ws)
+    if isolated:
+        # single-token candidates: each suffix row sees the prefix and itself
+        ws = torch.empty(max(1, api.load().bat_attn_isolated_workspace_size(
+            wl.B, wl.H, wl.D, api.BAT_BF16 if wl.dtype == "bf16" else api.BAT_F32, wl.total_s,
+            dw.max_s, dw.max_p)), dtype=torch.uint8, device="cuda")
+
+        def step():
+            api.attn_prefill_isolated(dw.q, dw.k, dw.v, dw.cu_s, dw.prefix_lens, dw.prefix_mode,
+                                      dw.block_table, 1, dw.user_pool, dw.item_pool, wl.scale,
+                                      dw.max_s, dw.max_p, out=out, lse=lse, workspace=ws)
+    else:
+        def step():
+            dw.run(out=out, lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -192,24 +205,27 @@ def main():
     ms_per_step = wall_s * 1e3 / args.steps
     flops = wl.flops()
     alg_bytes = wl.alg_bytes()
+    if isolated:  # each suffix row: its prefix plus one key
+        flops = float(4.0 * wl.D * wl.H * np.sum(wl.n_s.astype(np.float64) * (wl.n_p + 1)))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tok_s = wl.total_s / (ms_per_step * 1e-3)
     kernel_ms = float(per_call_ms.mean())
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    traffic = measured_traffic(wl.name, 1)
+    traffic = None if isolated else measured_traffic(wl.name, 1)
     props = torch.cuda.get_device_properties(0)
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events: mean "
           f"{kernel_ms:.4f}, min {per_call_ms.min():.4f}, p90 {np.percentile(per_call_ms, 90):.4f})"
           f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     base = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not isolated:
         base = run_cpu_baseline(wl, args.cpu_seconds)
 
     line = {
-        "metric": "prefill attention TFLOP/s (% bf16 MFMA peak) + suffix tokens/s, 1 GPU",
+        "metric": ("candidate-isolated prefill TFLOP/s, 1 GPU" if isolated else
+                   "prefill attention TFLOP/s (% bf16 MFMA peak) + suffix tokens/s, 1 GPU"),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -221,7 +237,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0,1) activations, shuffled paged prefix pool)",
-        "config": {"workload": f"{wl.name}: {wl.notes['description']}", "B": wl.B, "H": wl.H,
+        "config": {"workload": f"{wl.name}: {wl.notes['description']}"
+                               + ("; single-token candidates, each isolated" if isolated else ""),
+                   "B": wl.B, "H": wl.H,
                    "D": wl.D, "total_suffix": wl.total_s, "total_prefix": int(wl.n_p.sum()),
                    "user_block_size": wl.user_block_size, "seed": wl.seed},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2) if bf16 else None,
@@ -231,7 +249,8 @@ def main():
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
-                     "kernel": bf16_kernel_label(wl) if bf16 else f"attn_f32_kernel<{wl.D}>",
+                     "kernel": (bf16_kernel_label(wl) if bf16 else f"attn_f32_kernel<{wl.D}>")
+                               + (" + item_local_kernel (merge)" if isolated else ""),
                      "kernel_ms_mean": round(kernel_ms, 5)},
         "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
                      "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),

@@ -224,6 +224,56 @@ bat_status bat_attn_item_local(const void *q, const void *k, const void *v,
                                void *stream);
 
 /*
+ * bat_attn_isolated_workspace_size -- bytes of device workspace
+ * bat_attn_prefill_isolated needs (the work list plus one fp32 prefix
+ * partial per suffix row and head).  Returns 0 for invalid arguments.
+ */
+size_t bat_attn_isolated_workspace_size(int32_t B, int32_t H, int32_t D,
+                                        bat_dtype dt, int32_t total_suffix,
+                                        int32_t max_suffix_len,
+                                        int32_t max_prefix_len);
+
+/*
+ * bat_attn_prefill_isolated -- suffix rows over the cached prefix and their
+ * own candidate only (candidate-isolated suffix).
+ *
+ * The suffix of a recommendation request is a list of candidate items
+ * scored together (Bat page, "This paper's idea": the item tokens are the
+ * candidates; order-agnostic, so no positions).  Where candidates must be
+ * scored independently of one another, each candidate's T tokens see the
+ * request's prefix and themselves, not the other candidates: for a row i of
+ * candidate c of request r,
+ *     visible keys = P(r) + the T tokens of c,
+ *     lse_i = ln sum_visible exp(S_ij), out_i = sum_visible exp(S_ij - lse_i) v_j.
+ * Candidate c of request r is suffix rows cu_suffix_lens[r] + c*T ..
+ * + c*T + T-1; every request's suffix length must be a multiple of T (the
+ * result is unspecified otherwise).  Computed as the prefix part of every
+ * row (the attention kernels over the prefix only, fp32 partials in the
+ * workspace) merged exactly with each candidate's own part.
+ *
+ *   Arguments as bat_attn_prefill, plus
+ *   tokens_per_candidate  T, one of 1, 2, 4, 8 (else BAT_ERR_UNSUPPORTED);
+ *                   total_suffix must be a multiple of T
+ *   workspace       device, >= bat_attn_isolated_workspace_size(...) bytes
+ */
+bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v,
+                                     const int32_t *cu_suffix_lens,
+                                     const int32_t *prefix_lens,
+                                     const uint8_t *prefix_mode,
+                                     const int32_t *block_table,
+                                     int32_t bt_stride,
+                                     const bat_kv_pool *user_pool,
+                                     const bat_kv_pool *item_pool, int32_t B,
+                                     int32_t H, int32_t D, bat_dtype dt,
+                                     float softmax_scale,
+                                     int32_t tokens_per_candidate,
+                                     int32_t total_suffix,
+                                     int32_t max_suffix_len,
+                                     int32_t max_prefix_len, void *out,
+                                     float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * bat_lse_merge -- combine n_parts attention partials over disjoint key sets
  * into one result (the log-sum-exp merge; it is how a prefix split across
  * workgroups, or across devices, is recombined, and it is exact: merging the

@@ -22,7 +22,9 @@ hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_
                             int H, int D, bool bf16, void *out, float *lse, hipStream_t stream);
 hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_t n_items,
                              int32_t T, int32_t H, int32_t D, bool bf16, float scale_log2,
-                             void *out, float *lse, hipStream_t stream);
+                             void *out, float *lse, const float *o_p, const float *lse_p,
+                             const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
+                             int32_t max_prefix, hipStream_t stream);
 int bf16_rows_per_item(int W);
 int bf16_keys_per_tile(int D);
 int f32_rows_per_item();
@@ -70,8 +72,10 @@ struct Plan {
          total = 0;
 };
 
+// prefix_only: the rows see their prefix only and every row gets an fp32
+// partial (candidate-isolated suffixes); prefixes are then never split.
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
-               int32_t max_p, Plan &pl) {
+               int32_t max_p, Plan &pl, bool prefix_only = false) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
@@ -91,7 +95,9 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
   const int64_t target = 512;
   pl.chunk_len = 0;
-  if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
+  if (prefix_only) {
+    // one partial row per suffix row, no split
+  } else if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v > 0) pl.chunk_len = ((v + pl.bn - 1) / pl.bn) * pl.bn;
   } else if (lower_items > 0 && lower_items < target && max_p >= 2048) {
@@ -106,7 +112,8 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   const int64_t t_max = (max_s + pl.bm - 1) / pl.bm;
   const int64_t n_groups = (int64_t)H * B * pl.max_chunks;
   pl.grid = kNumXcd * ((n_groups + kNumXcd - 1) / kNumXcd) * t_max;
-  pl.part_rows = pl.max_chunks > 1 ? (int64_t)pl.max_chunks * total_s : 0;
+  pl.part_rows = prefix_only ? (int64_t)total_s
+                             : pl.max_chunks > 1 ? (int64_t)pl.max_chunks * total_s : 0;
   // the planner counts items and split-partial rows in 32 bits
   if (pl.grid > (int64_t)1 << 30 || pl.part_rows >= (int64_t)1 << 31) return false;
   size_t off = align256(kHdrWords * sizeof(int32_t));
@@ -213,7 +220,8 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
                      const bat_kv_pool *item_pool, int32_t B, int32_t H, int32_t D, bat_dtype dt,
                      float softmax_scale, int32_t total_suffix, int32_t max_suffix_len,
                      int32_t max_prefix_len, void *out, float *lse, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+                     size_t workspace_bytes, void *stream, bool prefix_only = false,
+                     const float **part_o = nullptr, const float **part_lse = nullptr) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -224,12 +232,15 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   if (max_prefix_len > 0 && p.pool_blocks[0] == 0 && p.pool_blocks[1] == 0)
     return BAT_ERR_INVALID_ARG;
   Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl))
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only))
     return BAT_ERR_INVALID_ARG;
   if (!workspace) return BAT_ERR_WORKSPACE;
   if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
 
   uint8_t *ws = (uint8_t *)workspace;
+  p.prefix_only = prefix_only ? 1 : 0;
+  if (part_o) *part_o = (const float *)(ws + pl.off_part_o);
+  if (part_lse) *part_lse = (const float *)(ws + pl.off_part_lse);
   int32_t *hdr = (int32_t *)ws;
   p.q = q;
   p.k = k;
@@ -263,7 +274,7 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, pl.flat_gather, (int)pl.grid, st)
                                       : launch_attn_f32(p, D, (int)pl.grid, st);
   if (e != hipSuccess) return BAT_ERR_HIP;
-  if (pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)
+  if (!prefix_only && pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)
     return BAT_ERR_HIP;
   if (val) {
     int32_t h_err = 0;
@@ -337,7 +348,58 @@ bat_status bat_attn_item_local(const void *q, const void *k, const void *v, int3
   if (n_items == 0) return BAT_OK;
   if (!q || !k || !v || !out) return BAT_ERR_INVALID_ARG;
   const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
-  if (launch_item_local(q, k, v, n_items, T, H, D, dt == BAT_BF16, scale_log2, out, lse,
+  if (launch_item_local(q, k, v, n_items, T, H, D, dt == BAT_BF16, scale_log2, out, lse, nullptr,
+                        nullptr, nullptr, nullptr, 0, 0, (hipStream_t)stream) != hipSuccess)
+    return BAT_ERR_HIP;
+  return BAT_OK;
+}
+
+size_t bat_attn_isolated_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
+                                        int32_t total_suffix, int32_t max_suffix_len,
+                                        int32_t max_prefix_len) {
+  Plan pl;
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, true)) return 0;
+  return pl.total;
+}
+
+bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v,
+                                     const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                                     const uint8_t *prefix_mode, const int32_t *block_table,
+                                     int32_t bt_stride, const bat_kv_pool *user_pool,
+                                     const bat_kv_pool *item_pool, int32_t B, int32_t H,
+                                     int32_t D, bat_dtype dt, float softmax_scale,
+                                     int32_t tokens_per_candidate, int32_t total_suffix,
+                                     int32_t max_suffix_len, int32_t max_prefix_len, void *out,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
+      bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  const int T = tokens_per_candidate;
+  if (!(T == 1 || T == 2 || T == 4 || T == 8)) return BAT_ERR_UNSUPPORTED;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix % T != 0 || (int64_t)(total_suffix / T) * H > 0x7fff0000)
+    return BAT_ERR_INVALID_ARG;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  const float *o_p = nullptr, *lse_p = nullptr;
+  if (max_prefix_len > 0) {
+    // the prefix part of every row, as fp32 partials in the workspace
+    const bat_status s = attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode,
+                                   block_table, bt_stride, user_pool, item_pool, B, H, D, dt,
+                                   softmax_scale, total_suffix, max_suffix_len, max_prefix_len,
+                                   out, lse, workspace, workspace_bytes, stream, true, &o_p,
+                                   &lse_p);
+    if (s != BAT_OK) return s;
+  }
+  // each candidate over its own tokens, merged with its row's prefix part
+  const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  if (launch_item_local(q, k, v, total_suffix / T, T, H, D, dt == BAT_BF16, scale_log2, out, lse,
+                        o_p, lse_p, cu_suffix_lens, prefix_lens, B, max_prefix_len,
                         (hipStream_t)stream) != hipSuccess)
     return BAT_ERR_HIP;
   return BAT_OK;

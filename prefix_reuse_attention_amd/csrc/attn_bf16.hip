@@ -587,6 +587,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  // prefix-only rows of a request with no prefix: no keys, nothing to write
+  // (the merge that follows reads that partial as empty)
+  if (n_tiles == 0) return;
   cp.n_tiles = n_tiles;
   __shared__ u32x4 s_tab[TileCopy<D, W, FLAT>::kTabTiles];
   cp.tab = s_tab;
@@ -656,7 +659,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   const float inv = 1.0f / l_tot;
   const float lse_nat = (sm.m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (!row_ok) return;
-  if (x.n_chunks <= 1) {
+  if (!x.partial) {
     uint16_t *out = (uint16_t *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D;
 #pragma unroll
     for (int nd = 0; nd < C::ND; ++nd)
@@ -765,6 +768,9 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
+  // prefix-only rows of a request with no prefix: no keys, nothing to write
+  // (the merge that follows reads that partial as empty)
+  if (n_tiles == 0) return;
   cp.n_tiles = n_tiles;
   cp.tab = s_tab;
   cp.use_tab = n_tiles <= TC::kTabTiles;
@@ -1032,7 +1038,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   const float inv = 1.0f / l_tot;
   const float lse_nat = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (!row_ok) return;
-  if (x.n_chunks <= 1) {
+  if (!x.partial) {
     uint16_t *out = (uint16_t *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D;
 #pragma unroll
     for (int nd = 0; nd < C::ND; ++nd)

@@ -45,6 +45,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   const int n_pkeys = x.p_end - x.p_begin;
   const int n_tiles_p = (n_pkeys + kF32Keys - 1) / kF32Keys;
   const int n_tiles = n_tiles_p + (x.with_suffix ? (x.n_s + kF32Keys - 1) / kF32Keys : 0);
+  // prefix-only rows of a request with no prefix: no keys, nothing to write
+  // (the merge that follows reads that partial as empty)
+  if (n_tiles == 0) return;
   constexpr int V4_PER_ROW = D / 4;
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   if (!row_ok) return;
   const float inv = 1.0f / l_run;
   const float lse_nat = (m_run + log2f(l_run)) * 0.69314718055994530942f;
-  if (x.n_chunks <= 1) {
+  if (!x.partial) {
     float *op = (float *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D + part * DQ;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) op[d] = o[d] * inv;

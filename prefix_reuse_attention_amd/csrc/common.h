@@ -55,6 +55,8 @@ struct AttnParams {
   int32_t total_s;
   float scale_log2;               // softmax_scale * log2(e)
   int32_t chunk_len;              // prefix keys per chunk when split (0 = never)
+  int32_t prefix_only;            // 1: rows see the prefix only; the kernels write fp32
+                                  // partials at part_o / part_lse row q0 + row
   int32_t max_prefix;             // host bound; longer prefixes are clamped to it
   const WorkItem *items;
   const ReqMeta *meta;
@@ -70,6 +72,7 @@ struct AttnParams {
 struct ItemRange {
   int32_t q0, n_s, n_p, mode, p_begin, p_end, n_chunks, part_off;
   bool with_suffix;
+  bool partial;  // write an fp32 partial (split chunk, or prefix-only rows)
 };
 
 __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) {
@@ -90,6 +93,12 @@ __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) 
     x.p_begin = it.chunk * p.chunk_len;
     x.p_end = min(x.n_p, x.p_begin + p.chunk_len);
     x.with_suffix = it.chunk == x.n_chunks - 1;
+  }
+  x.partial = x.n_chunks > 1;
+  if (p.prefix_only) {  // never split: one partial row per suffix row
+    x.with_suffix = false;
+    x.partial = true;
+    x.part_off = x.q0;
   }
   return x;
 }

@@ -18,6 +18,15 @@
 // lane then holds the item's T*T scores, takes the softmax in fp32 and writes
 // its slice of the T output rows.  T*T and G are small, so the kernel is
 // bound by the 3*T reads and T writes of D elements per (item, head).
+//
+// The same kernel finishes candidate-isolated suffix rows (MERGE): there the
+// "items" are a request's suffix candidates of T tokens, each row sees its
+// request's prefix plus its own candidate, and the prefix part arrives as an
+// fp32 partial (output normalised over the prefix and its log-sum-exp) from
+// the attention kernels run over the prefix only.  The two partials over
+// disjoint keys combine exactly: lse = ln(e^lse_p + e^lse_c),
+// out = e^(lse_p - lse) out_p + e^(lse_c - lse) out_c.  A request with no
+// prefix has no partial; its rows keep the candidate part alone.
 #include "common.h"
 
 namespace bat {
@@ -40,13 +49,23 @@ struct Slice {
   }
 };
 
-template <int D, int T, bool BF16>
+// The prefix partial of candidate-isolated rows (MERGE only).
+struct PrefixPartial {
+  const float *o;              // [rows, H, D] fp32, normalised over the prefix
+  const float *lse;            // [rows, H] natural log
+  const int32_t *cu_s;         // [B+1] rows of each request
+  const int32_t *prefix_lens;  // [B]
+  int32_t B, max_prefix;
+};
+
+template <int D, int T, bool BF16, bool MERGE>
 __global__ __launch_bounds__(256) void item_local_kernel(const void *__restrict__ q,
                                                          const void *__restrict__ k,
                                                          const void *__restrict__ v,
                                                          int32_t n_items, int32_t H,
                                                          float scale_log2, void *__restrict__ out,
-                                                         float *__restrict__ lse) {
+                                                         float *__restrict__ lse,
+                                                         PrefixPartial pp) {
   using S = Slice<BF16>;
   constexpr int EB = BF16 ? 2 : 4;  // bytes per element
   constexpr int G = D / S::N;       // lanes per (item, head)
@@ -88,6 +107,20 @@ __global__ __launch_bounds__(256) void item_local_kernel(const void *__restrict_
 #pragma unroll
       for (int b = 0; b < T; ++b) s[a][b] += __shfl_xor(s[a][b], m, G);
 
+  // MERGE: whether this candidate's request has a prefix partial (the
+  // candidates of a request start at multiples of T, so one lookup serves all
+  // T rows)
+  bool has_prefix = false;
+  if constexpr (MERGE) {
+    int lo = 0, hi = pp.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pp.cu_s[mid] <= row0) lo = mid; else hi = mid - 1;
+    }
+    const int n_p = pp.prefix_lens ? min(max(pp.prefix_lens[lo], 0), pp.max_prefix) : 0;
+    has_prefix = n_p > 0;
+  }
+
   // softmax per row in the log2 domain, then this lane's slice of the output
   const int64_t total = (int64_t)n_items * T;
 #pragma unroll
@@ -111,6 +144,24 @@ __global__ __launch_bounds__(256) void item_local_kernel(const void *__restrict_
       for (int b = 0; b < T; ++b) acc = __builtin_fmaf(p[b], vs[b].at(e), acc);
       o[e] = acc * inv;
     }
+    float lse2 = m2 + __log2f(l);  // this row's log-sum-exp, log2 domain
+    if constexpr (MERGE) {
+      if (has_prefix) {
+        const int64_t pr = (row0 + a) * H + head;
+        const float lp = pp.lse[pr] * 1.44269504088896340736f;
+        const float mx = fmaxf(lp, lse2);
+        const float wp = __builtin_amdgcn_exp2f(lp - mx), wc = __builtin_amdgcn_exp2f(lse2 - mx);
+        const float iw = 1.0f / (wp + wc);
+        const f32x4 *po = (const f32x4 *)(pp.o + pr * D + (int64_t)c * S::N);
+#pragma unroll
+        for (int e4 = 0; e4 < S::N / 4; ++e4) {
+          const f32x4 x = po[e4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[4 * e4 + i] = (wp * x[i] + wc * o[4 * e4 + i]) * iw;
+        }
+        lse2 = mx + __log2f(wp + wc);
+      }
+    }
     const int64_t off = (((row0 + a) * H + head) * D + (int64_t)c * S::N) * EB;
     if constexpr (BF16) {
       typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -122,48 +173,58 @@ __global__ __launch_bounds__(256) void item_local_kernel(const void *__restrict_
       const f32x4 f = {o[0], o[1], o[2], o[3]};
       *(f32x4 *)((uint8_t *)out + off) = f;
     }
-    if (lse && c == 0) lse[(int64_t)head * total + row0 + a] = (m2 + __log2f(l)) * 0.69314718055994530942f;
+    if (lse && c == 0) lse[(int64_t)head * total + row0 + a] = lse2 * 0.69314718055994530942f;
   }
 }
 
 template <int D, int T, bool BF16>
 hipError_t launch_item_local_t(const void *q, const void *k, const void *v, int32_t n_items,
                                int32_t H, float scale_log2, void *out, float *lse,
-                               hipStream_t stream) {
+                               const PrefixPartial *pp, hipStream_t stream) {
   constexpr int G = D / (BF16 ? 8 : 4);
   constexpr int groups_per_block = 4 * (kWave / G);  // four waves
   const int64_t groups = (int64_t)n_items * H;
   if (groups > 0x7fffffff - groups_per_block) return hipErrorInvalidValue;
   const int64_t blocks = (groups + groups_per_block - 1) / groups_per_block;
-  hipLaunchKernelGGL((item_local_kernel<D, T, BF16>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, q, k, v, n_items, H, scale_log2, out, lse);
+  if (pp)
+    hipLaunchKernelGGL((item_local_kernel<D, T, BF16, true>), dim3((unsigned)blocks), dim3(256),
+                       0, stream, q, k, v, n_items, H, scale_log2, out, lse, *pp);
+  else
+    hipLaunchKernelGGL((item_local_kernel<D, T, BF16, false>), dim3((unsigned)blocks), dim3(256),
+                       0, stream, q, k, v, n_items, H, scale_log2, out, lse, PrefixPartial{});
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_item_local_d(const void *q, const void *k, const void *v, int32_t n_items,
                                int32_t T, int32_t H, float scale_log2, void *out, float *lse,
-                               hipStream_t stream) {
+                               const PrefixPartial *pp, hipStream_t stream) {
   switch (T) {
-    case 1: return launch_item_local_t<D, 1, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
-    case 2: return launch_item_local_t<D, 2, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
-    case 4: return launch_item_local_t<D, 4, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
-    case 8: return launch_item_local_t<D, 8, BF16>(q, k, v, n_items, H, scale_log2, out, lse, stream);
+    case 1: return launch_item_local_t<D, 1, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
+    case 2: return launch_item_local_t<D, 2, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
+    case 4: return launch_item_local_t<D, 4, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
+    case 8: return launch_item_local_t<D, 8, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
   }
   return hipErrorInvalidValue;
 }
 
 // Tokens per item T in {1, 2, 4, 8}; (dtype, D) as the attention kernels.
+// With a prefix partial (o_p non-null) the items are suffix candidates and
+// the result is merged with it.
 hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_t n_items,
                              int32_t T, int32_t H, int32_t D, bool bf16, float scale_log2,
-                             void *out, float *lse, hipStream_t stream) {
+                             void *out, float *lse, const float *o_p, const float *lse_p,
+                             const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
+                             int32_t max_prefix, hipStream_t stream) {
+  const PrefixPartial part{o_p, lse_p, cu_s, prefix_lens, B, max_prefix};
+  const PrefixPartial *pp = o_p ? &part : nullptr;
   if (bf16) {
-    if (D == 64) return launch_item_local_d<64, true>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
-    if (D == 128) return launch_item_local_d<128, true>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+    if (D == 64) return launch_item_local_d<64, true>(q, k, v, n_items, T, H, scale_log2, out, lse, pp, stream);
+    if (D == 128) return launch_item_local_d<128, true>(q, k, v, n_items, T, H, scale_log2, out, lse, pp, stream);
   } else {
-    if (D == 32) return launch_item_local_d<32, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
-    if (D == 64) return launch_item_local_d<64, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
-    if (D == 128) return launch_item_local_d<128, false>(q, k, v, n_items, T, H, scale_log2, out, lse, stream);
+    if (D == 32) return launch_item_local_d<32, false>(q, k, v, n_items, T, H, scale_log2, out, lse, pp, stream);
+    if (D == 64) return launch_item_local_d<64, false>(q, k, v, n_items, T, H, scale_log2, out, lse, pp, stream);
+    if (D == 128) return launch_item_local_d<128, false>(q, k, v, n_items, T, H, scale_log2, out, lse, pp, stream);
   }
   return hipErrorInvalidValue;
 }

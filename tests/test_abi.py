@@ -194,6 +194,50 @@ def test_item_local_argument_errors(lib, over, status):
     assert item_local(lib, **over) == status
 
 
+def isolated(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, plen=FAKE, mode=FAKE, bt=FAKE, bt_stride=16,
+             up=_pool(), ip=None, B=2, H=8, D=64, dt=api.BAT_BF16, scale=0.125, T=4, total=1024,
+             max_s=512, max_p=1024, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    up = ctypes.byref(a["up"]) if a["up"] is not None else None
+    ip = ctypes.byref(a["ip"]) if a["ip"] is not None else None
+    if a["ws_bytes"] == "exact-1":
+        a["ws_bytes"] = lib.bat_attn_isolated_workspace_size(a["B"], a["H"], a["D"], a["dt"],
+                                                             a["total"], a["max_s"],
+                                                             a["max_p"]) - 1
+    return lib.bat_attn_prefill_isolated(a["q"], a["k"], a["v"], a["cu"], a["plen"], a["mode"],
+                                         a["bt"], a["bt_stride"], up, ip, a["B"], a["H"], a["D"],
+                                         a["dt"], a["scale"], a["T"], a["total"], a["max_s"],
+                                         a["max_p"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), api.BAT_ERR_INVALID_ARG),
+    (dict(plen=None), api.BAT_ERR_INVALID_ARG),
+    (dict(bt=None), api.BAT_ERR_INVALID_ARG),          # prefixes but no block table
+    (dict(up=None), api.BAT_ERR_INVALID_ARG),          # prefixes but no pool
+    (dict(scale=0.0), api.BAT_ERR_INVALID_ARG),
+    (dict(T=3), api.BAT_ERR_UNSUPPORTED),
+    (dict(T=16), api.BAT_ERR_UNSUPPORTED),
+    (dict(total=1022), api.BAT_ERR_INVALID_ARG),       # not whole candidates
+    (dict(D=32), api.BAT_ERR_UNSUPPORTED),
+    (dict(ws=None), api.BAT_ERR_WORKSPACE),
+    (dict(ws_bytes="exact-1"), api.BAT_ERR_WORKSPACE),
+    (dict(total=0), api.BAT_OK),
+])
+def test_isolated_argument_errors(lib, over, status):
+    assert isolated(lib, **over) == status
+
+
+def test_isolated_workspace_holds_a_partial_per_row(lib):
+    f, g = lib.bat_attn_isolated_workspace_size, lib.bat_attn_workspace_size
+    # one fp32 output row and lse per (suffix row, head) beyond the work list
+    assert f(2, 8, 64, api.BAT_BF16, 1024, 512, 1024) >= \
+        g(2, 8, 64, api.BAT_BF16, 1024, 512, 1024) + 1024 * 8 * (64 + 1) * 4
+    assert f(2, 8, 96, api.BAT_BF16, 1024, 512, 1024) == 0
+
+
 def test_lse_merge_argument_errors(lib):
     m = lib.bat_lse_merge
     assert m(FAKE, FAKE, 0, 10, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG

@@ -192,6 +192,24 @@ def item_local(q, k, v, tokens_per_item, scale, rows=None, heads=None):
     return prefill_suffix(q, k, v, cu, empty, empty, zeros, scale, rows, heads)
 
 
+def prefill_suffix_gqa(q, k_s, v_s, cu_s, k_p, v_p, cu_p, scale, rows=None, heads=None):
+    """prefill_suffix with grouped key/value heads, float64.
+
+    q is [total_s, H, D]; k_s/v_s and k_p/v_p carry H_kv heads, H a multiple
+    of H_kv.  Query head h attends with key/value head h // (H // H_kv):
+    that is the plain prefill over key/value heads repeated H // H_kv times
+    each, which is how it is computed here.
+    """
+    H = np.asarray(q).shape[1]
+    H_kv = np.asarray(k_s).shape[1]
+    if H % H_kv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    g = H // H_kv
+    rep = lambda x: np.repeat(np.asarray(x), g, axis=1)
+    return prefill_suffix(q, rep(k_s), rep(v_s), cu_s, rep(k_p), rep(v_p), cu_p, scale,
+                          rows, heads)
+
+
 def _widen(x):
     """float64 values of a float32 or bf16-bits (uint16) array, exactly."""
     x = np.asarray(x)

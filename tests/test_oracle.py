@@ -514,3 +514,42 @@ def test_isolated_selected_rows_match_full():
                                      heads=heads)
     np.testing.assert_array_equal(so, out[rows, heads])
     np.testing.assert_array_equal(sl, lse[heads, rows])
+
+
+# ------------------------------------------------------ grouped key/value heads
+def test_gqa_library_sdpa():
+    """Grouped heads equal torch SDPA with enable_gqa (one request: suffix rows
+    over prefix + suffix keys, no mask)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    rng = np.random.default_rng(41)
+    n_p, n_s, H, H_kv, D = 13, 6, 8, 2, 16
+    q = rng.standard_normal((n_s, H, D))
+    k_s, v_s = rng.standard_normal((n_s, H_kv, D)), rng.standard_normal((n_s, H_kv, D))
+    k_p, v_p = rng.standard_normal((n_p, H_kv, D)), rng.standard_normal((n_p, H_kv, D))
+    scale = 1.0 / math.sqrt(D)
+    out, _ = oracle.prefill_suffix_gqa(q, k_s, v_s, np.array([0, n_s], np.int32), k_p, v_p,
+                                       np.array([0, n_p], np.int32), scale)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x.transpose(1, 0, 2)))[None]
+    kk, vv = np.concatenate([k_p, k_s]), np.concatenate([v_p, v_s])
+    ref = F.scaled_dot_product_attention(t(q), t(kk), t(vv), scale=scale, enable_gqa=True)[0]
+    np.testing.assert_allclose(out, ref.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def test_gqa_brute_force_head_mapping():
+    """Explicit loops: query head h uses key/value head h // (H // H_kv)."""
+    rng = np.random.default_rng(42)
+    n_p, n_s, H, H_kv, D, scale = 3, 2, 4, 2, 3, 0.6
+    q = rng.standard_normal((n_s, H, D))
+    k_s, v_s = rng.standard_normal((n_s, H_kv, D)), rng.standard_normal((n_s, H_kv, D))
+    k_p, v_p = rng.standard_normal((n_p, H_kv, D)), rng.standard_normal((n_p, H_kv, D))
+    out, lse = oracle.prefill_suffix_gqa(q, k_s, v_s, np.array([0, n_s], np.int32), k_p, v_p,
+                                         np.array([0, n_p], np.int32), scale)
+    for h in range(H):
+        g = h // (H // H_kv)
+        kk = np.concatenate([k_p[:, g], k_s[:, g]])
+        vv = np.concatenate([v_p[:, g], v_s[:, g]])
+        bo, bl = brute_force(np.concatenate([np.zeros((n_p, D)), q[:, h]]), kk, vv,
+                             np.array([True] * n_p + [False] * n_s), scale)
+        np.testing.assert_allclose(out[:, h], bo[n_p:], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h], bl[n_p:], rtol=0, atol=1e-12)

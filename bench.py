@@ -100,11 +100,13 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--workload", choices=("prefill", "isolated", "prefix-rows", "item-local"),
+    ap.add_argument("--workload", choices=("prefill", "isolated", "gqa", "prefix-rows",
+                                           "item-local"),
                     default="prefill",
                     help="prefill: bat_attn_prefill on --config (the default line); "
                          "isolated: bat_attn_prefill_isolated on --config with single-token "
-                         "candidates; prefix-rows: bat_attn_prefix_rows over the 8k-history "
+                         "candidates; gqa: bat_attn_prefill_gqa on the 8k-history shape with 4 "
+                         "key/value heads for its 16 query heads; prefix-rows: bat_attn_prefix_rows over the 8k-history "
                          "prefixes; item-local: bat_attn_item_local over the 20000-item pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -148,8 +150,17 @@ def main():
         bench_prefix_workload(args)
         return
     isolated = args.workload == "isolated"
+    gqa_heads = 0
     t0 = time.time()
-    wl = W.make_config(args.config)
+    if args.workload == "gqa":
+        # the 8k-history shape: 16 query heads over 4 key/value heads
+        gqa_heads = 16
+        wl = W.make_custom(dtype="bf16", H=4, D=128, n_s=[512] * 16, n_p=[8192] * 16,
+                           mode=[W.USER] * 16, seed=104, user_block_size=64, name="config4_gqa")
+        wl.notes["description"] = ("bf16, B=16, 16 query heads over 4 key/value heads, D=128, "
+                                   "user prefix 8192 (64-token pages), suffix 512")
+    else:
+        wl = W.make_config(args.config)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",
           file=sys.stderr, flush=True)
 
@@ -173,6 +184,15 @@ def main():
     ws = dw.workspace()
     out = torch.empty_like(dw.q)
     lse = torch.empty((wl.H, wl.total_s), dtype=torch.float32, device="cuda")
+    if gqa_heads:
+        from prefix_reuse_attention_amd.device import to_device
+        q_big = to_device(W._normal(np.random.default_rng(105), (wl.total_s, gqa_heads, wl.D),
+                                    "bf16"), "bf16")
+        out = torch.empty_like(q_big)
+        lse = torch.empty((gqa_heads, wl.total_s), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, api.load().bat_attn_gqa_workspace_size(
+            wl.B, gqa_heads, wl.H, wl.D, api.BAT_BF16, wl.total_s, dw.max_s, dw.max_p)),
+            dtype=torch.uint8, device="cuda")
 
     if isolated:
         # single-token candidates: each suffix row sees the prefix and itself
@@ -184,6 +204,11 @@ def main():
             api.attn_prefill_isolated(dw.q, dw.k, dw.v, dw.cu_s, dw.prefix_lens, dw.prefix_mode,
                                       dw.block_table, 1, dw.user_pool, dw.item_pool, wl.scale,
                                       dw.max_s, dw.max_p, out=out, lse=lse, workspace=ws)
+    elif gqa_heads:
+        def step():
+            api.attn_prefill_gqa(q_big, dw.k, dw.v, dw.cu_s, dw.prefix_lens, dw.prefix_mode,
+                                 dw.block_table, dw.user_pool, dw.item_pool, wl.scale, dw.max_s,
+                                 dw.max_p, out=out, lse=lse, workspace=ws)
     else:
         def step():
             dw.run(out=out, lse=lse, workspace=ws)
@@ -205,6 +230,8 @@ def main():
     ms_per_step = wall_s * 1e3 / args.steps
     flops = wl.flops()
     alg_bytes = wl.alg_bytes()
+    if gqa_heads:  # the work of the query heads
+        flops = flops * gqa_heads / wl.H
     if isolated:  # each suffix row: its prefix plus one key
         flops = float(4.0 * wl.D * wl.H * np.sum(wl.n_s.astype(np.float64) * (wl.n_p + 1)))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -213,18 +240,19 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    traffic = None if isolated else measured_traffic(wl.name, 1)
+    traffic = None if (isolated or gqa_heads) else measured_traffic(wl.name, 1)
     props = torch.cuda.get_device_properties(0)
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events: mean "
           f"{kernel_ms:.4f}, min {per_call_ms.min():.4f}, p90 {np.percentile(per_call_ms, 90):.4f})"
           f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     base = None
-    if not args.no_cpu_baseline and not isolated:
+    if not args.no_cpu_baseline and not isolated and not gqa_heads:
         base = run_cpu_baseline(wl, args.cpu_seconds)
 
     line = {
         "metric": ("candidate-isolated prefill TFLOP/s, 1 GPU" if isolated else
+                   "grouped-head prefill TFLOP/s, 1 GPU" if gqa_heads else
                    "prefill attention TFLOP/s (% bf16 MFMA peak) + suffix tokens/s, 1 GPU"),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
@@ -239,7 +267,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, shuffled paged prefix pool)",
         "config": {"workload": f"{wl.name}: {wl.notes['description']}"
                                + ("; single-token candidates, each isolated" if isolated else ""),
-                   "B": wl.B, "H": wl.H,
+                   "B": wl.B, "H": gqa_heads or wl.H,
+                   **({"H_kv": wl.H} if gqa_heads else {}),
                    "D": wl.D, "total_suffix": wl.total_s, "total_prefix": int(wl.n_p.sum()),
                    "user_block_size": wl.user_block_size, "seed": wl.seed},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2) if bf16 else None,

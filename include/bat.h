@@ -224,6 +224,50 @@ bat_status bat_attn_item_local(const void *q, const void *k, const void *v,
                                void *stream);
 
 /*
+ * bat_attn_gqa_workspace_size -- bytes of device workspace
+ * bat_attn_prefill_gqa needs.  Returns 0 for invalid arguments (including
+ * H not a multiple of H_kv).
+ */
+size_t bat_attn_gqa_workspace_size(int32_t B, int32_t H, int32_t H_kv,
+                                   int32_t D, bat_dtype dt,
+                                   int32_t total_suffix,
+                                   int32_t max_suffix_len,
+                                   int32_t max_prefix_len);
+
+/*
+ * bat_attn_prefill_gqa -- bat_attn_prefill with grouped key/value heads.
+ *
+ * H query heads share H_kv key/value heads (H a multiple of H_kv): query
+ * head h attends with key/value head h / (H / H_kv); everything else is
+ * bat_attn_prefill's definition (the pages fix no head layout; this is the
+ * grouped form of the same attention, with a cache H / H_kv times smaller).
+ *
+ *   q, out          device [total_suffix, H, D]; lse [H, total_suffix]
+ *   k, v            device, packed fresh suffix [total_suffix, H_kv, D]
+ *   user_pool, item_pool  pools of H_kv heads: [num_blocks, H_kv, bs, D]
+ *                   (bat_kv_build with H = H_kv builds them)
+ *   H, H_kv         query and key/value heads; H % H_kv == 0, else
+ *                   BAT_ERR_INVALID_ARG
+ *   workspace       >= bat_attn_gqa_workspace_size(B, H, H_kv, ...) bytes
+ * Other arguments, dtypes and head dims as bat_attn_prefill.  The work of
+ * the query heads that share a key/value head is placed on one XCD so that
+ * their key/value tiles are read from HBM once.
+ */
+bat_status bat_attn_prefill_gqa(const void *q, const void *k, const void *v,
+                                const int32_t *cu_suffix_lens,
+                                const int32_t *prefix_lens,
+                                const uint8_t *prefix_mode,
+                                const int32_t *block_table, int32_t bt_stride,
+                                const bat_kv_pool *user_pool,
+                                const bat_kv_pool *item_pool, int32_t B,
+                                int32_t H, int32_t H_kv, int32_t D,
+                                bat_dtype dt, float softmax_scale,
+                                int32_t total_suffix, int32_t max_suffix_len,
+                                int32_t max_prefix_len, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
  * bat_attn_isolated_workspace_size -- bytes of device workspace
  * bat_attn_prefill_isolated needs (the work list plus one fp32 prefix
  * partial per suffix row and head).  Returns 0 for invalid arguments.

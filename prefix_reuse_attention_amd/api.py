@@ -19,7 +19,8 @@ BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 
 EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill",
             "bat_attn_prefix_rows", "bat_attn_item_local", "bat_attn_isolated_workspace_size",
-            "bat_attn_prefill_isolated", "bat_lse_merge",
+            "bat_attn_prefill_isolated", "bat_attn_gqa_workspace_size", "bat_attn_prefill_gqa",
+            "bat_lse_merge",
             "bat_status_string", "bat_version")
 
 _lib = None
@@ -64,6 +65,11 @@ def load():
     lib.bat_attn_prefill_isolated.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I,
                                               I, I, P, P, P, ctypes.c_size_t, P]
     lib.bat_attn_prefill_isolated.restype = I
+    lib.bat_attn_gqa_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.bat_attn_gqa_workspace_size.restype = ctypes.c_size_t
+    lib.bat_attn_prefill_gqa.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, I, F, I,
+                                         I, I, P, P, P, ctypes.c_size_t, P]
+    lib.bat_attn_prefill_gqa.restype = I
     lib.bat_lse_merge.argtypes = [P, P, I, I, I, I, I, P, P, P]
     lib.bat_lse_merge.restype = I
     lib.bat_status_string.argtypes = [I]
@@ -274,6 +280,53 @@ def attn_item_local(q, k, v, tokens_per_item, softmax_scale=None, out=None, lse=
                                     _dtype_code(q), float(softmax_scale), _ptr(out), _ptr(lse),
                                     _stream())
     _check(st, "bat_attn_item_local")
+    return out, lse
+
+
+def attn_prefill_gqa(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
+                     user_pool=None, item_pool=None, softmax_scale=None, max_suffix_len=None,
+                     max_prefix_len=None, out=None, lse=None, workspace=None, want_lse=False):
+    """attn_prefill with grouped key/value heads: q is [total, H, D], k/v and
+    the pools carry H_kv heads (H a multiple of H_kv)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(cu_suffix_lens, "cu_suffix_lens", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    _need(prefix_mode, "prefix_mode", torch.uint8)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32)
+    total, H, D = q.shape
+    H_kv = k.shape[1]
+    B = cu_suffix_lens.shape[0] - 1
+    if max_suffix_len is None:
+        max_suffix_len = int((cu_suffix_lens[1:] - cu_suffix_lens[:-1]).max().item()) if B else 0
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_lens.max().item()) if B else 0
+    if softmax_scale is None:
+        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    ws_bytes = int(load().bat_attn_gqa_workspace_size(B, H, H_kv, D, dt, total, max_suffix_len,
+                                                       max_prefix_len))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    up = user_pool.struct() if user_pool is not None else None
+    ip = item_pool.struct() if item_pool is not None else None
+    st = load().bat_attn_prefill_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_suffix_lens), _ptr(prefix_lens), _ptr(prefix_mode),
+        _ptr(block_table), 0 if block_table is None else block_table.shape[1],
+        ctypes.byref(up) if up is not None else None,
+        ctypes.byref(ip) if ip is not None else None,
+        B, H, H_kv, D, dt, float(softmax_scale), total, int(max_suffix_len), int(max_prefix_len),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "bat_attn_prefill_gqa")
     return out, lse
 
 

@@ -11,7 +11,7 @@ hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu, cons
                            int elem_bytes, void *pk, void *pv, int32_t num_blocks,
                            int32_t bs_log2, int32_t *err, hipStream_t stream);
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B, int32_t H,
-                       int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
+                       int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
                        int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
                        hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
@@ -74,8 +74,9 @@ struct Plan {
 
 // prefix_only: the rows see their prefix only and every row gets an fp32
 // partial (candidate-isolated suffixes); prefixes are then never split.
+// hg: query heads per key/value head (grouped heads; 1 otherwise).
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
-               int32_t max_p, Plan &pl, bool prefix_only = false) {
+               int32_t max_p, Plan &pl, bool prefix_only = false, int32_t hg = 1) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
@@ -109,9 +110,12 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   }
   pl.max_chunks = (pl.chunk_len > 0 && max_p > pl.chunk_len)
                       ? (max_p + pl.chunk_len - 1) / pl.chunk_len : 1;
+  // a group is one (request, key/value head, chunk): hg query heads times
+  // up to t_max row tiles, all on one XCD
+  if (hg <= 0 || H % hg != 0) return false;
   const int64_t t_max = (max_s + pl.bm - 1) / pl.bm;
-  const int64_t n_groups = (int64_t)H * B * pl.max_chunks;
-  pl.grid = kNumXcd * ((n_groups + kNumXcd - 1) / kNumXcd) * t_max;
+  const int64_t n_groups = (int64_t)(H / hg) * B * pl.max_chunks;
+  pl.grid = kNumXcd * ((n_groups + kNumXcd - 1) / kNumXcd) * hg * t_max;
   pl.part_rows = prefix_only ? (int64_t)total_s
                              : pl.max_chunks > 1 ? (int64_t)pl.max_chunks * total_s : 0;
   // the planner counts items and split-partial rows in 32 bits
@@ -221,7 +225,8 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
                      float softmax_scale, int32_t total_suffix, int32_t max_suffix_len,
                      int32_t max_prefix_len, void *out, float *lse, void *workspace,
                      size_t workspace_bytes, void *stream, bool prefix_only = false,
-                     const float **part_o = nullptr, const float **part_lse = nullptr) {
+                     const float **part_o = nullptr, const float **part_lse = nullptr,
+                     int32_t H_kv = 0) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -231,8 +236,9 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   }
   if (max_prefix_len > 0 && p.pool_blocks[0] == 0 && p.pool_blocks[1] == 0)
     return BAT_ERR_INVALID_ARG;
+  const int32_t hg = H_kv > 0 ? H / H_kv : 1;
   Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only))
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only, hg))
     return BAT_ERR_INVALID_ARG;
   if (!workspace) return BAT_ERR_WORKSPACE;
   if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
@@ -252,6 +258,7 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   p.bt_stride = bt_stride;
   p.B = B;
   p.H = H;
+  p.H_kv = H_kv > 0 ? H_kv : H;
   p.total_s = total_suffix;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   p.chunk_len = pl.chunk_len;
@@ -266,7 +273,7 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   p.part_lse = (float *)(ws + pl.off_part_lse);
 
   hipStream_t st = (hipStream_t)stream;
-  if (launch_plan(cu_suffix_lens, prefix_lens, B, H, pl.bm, pl.chunk_len, max_prefix_len,
+  if (launch_plan(cu_suffix_lens, prefix_lens, B, H, hg, pl.bm, pl.chunk_len, max_prefix_len,
                   (int32_t)pl.grid, (int32_t *)(ws + pl.off_scratch),
                   (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
                   st) != hipSuccess)
@@ -352,6 +359,41 @@ bat_status bat_attn_item_local(const void *q, const void *k, const void *v, int3
                         nullptr, nullptr, nullptr, 0, 0, (hipStream_t)stream) != hipSuccess)
     return BAT_ERR_HIP;
   return BAT_OK;
+}
+
+size_t bat_attn_gqa_workspace_size(int32_t B, int32_t H, int32_t H_kv, int32_t D, bat_dtype dt,
+                                   int32_t total_suffix, int32_t max_suffix_len,
+                                   int32_t max_prefix_len) {
+  if (H_kv <= 0 || H % H_kv != 0) return 0;
+  Plan pl;
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, false, H / H_kv))
+    return 0;
+  return pl.total;
+}
+
+bat_status bat_attn_prefill_gqa(const void *q, const void *k, const void *v,
+                                const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                                const uint8_t *prefix_mode, const int32_t *block_table,
+                                int32_t bt_stride, const bat_kv_pool *user_pool,
+                                const bat_kv_pool *item_pool, int32_t B, int32_t H,
+                                int32_t H_kv, int32_t D, bat_dtype dt, float softmax_scale,
+                                int32_t total_suffix, int32_t max_suffix_len,
+                                int32_t max_prefix_len, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || total_suffix < 0 ||
+      max_suffix_len < 0 || max_prefix_len < 0 || bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  return attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table, bt_stride,
+                   user_pool, item_pool, B, H, D, dt, softmax_scale, total_suffix, max_suffix_len,
+                   max_prefix_len, out, lse, workspace, workspace_bytes, stream, false, nullptr,
+                   nullptr, H_kv);
 }
 
 size_t bat_attn_isolated_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,

@@ -570,8 +570,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.lg = p.pool_bs_log2[x.mode];
   cp.blocks = p.pool_blocks[x.mode];
   cp.bt_stride = p.bt_stride;
-  cp.H = p.H;
-  cp.head = head;
+  cp.H = p.H_kv;                       // the copies read key/value heads
+  cp.head = head / (p.H / p.H_kv);
   cp.q0 = x.q0;
   // suffix rows that lie past total_s (inconsistent lengths) are never read
   cp.n_s = (x.q0 >= 0) ? min(x.n_s, p.total_s - x.q0) : 0;
@@ -582,8 +582,8 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.wave = wave;
   cp.lane = lane;
   cp.whole_blocks = (1 << cp.lg) >= C::BN;
-  cp.block_bytes = (int64_t)p.H * ((int64_t)C::RB << cp.lg);
-  cp.head_bytes = (int64_t)head * ((int64_t)C::RB << cp.lg);
+  cp.block_bytes = (int64_t)p.H_kv * ((int64_t)C::RB << cp.lg);
+  cp.head_bytes = (int64_t)cp.head * ((int64_t)C::RB << cp.lg);
   cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
@@ -752,8 +752,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   cp.lg = p.pool_bs_log2[x.mode];
   cp.blocks = p.pool_blocks[x.mode];
   cp.bt_stride = p.bt_stride;
-  cp.H = p.H;
-  cp.head = head;
+  cp.H = p.H_kv;                       // the copies read key/value heads
+  cp.head = head / (p.H / p.H_kv);
   cp.q0 = x.q0;
   cp.n_s = (x.q0 >= 0) ? min(x.n_s, p.total_s - x.q0) : 0;
   cp.p_begin = x.p_begin;
@@ -763,8 +763,8 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   cp.wave = wave & 3;
   cp.lane = lane;
   cp.whole_blocks = (1 << cp.lg) >= C::BN;
-  cp.block_bytes = (int64_t)p.H * ((int64_t)C::RB << cp.lg);
-  cp.head_bytes = (int64_t)head * ((int64_t)C::RB << cp.lg);
+  cp.block_bytes = (int64_t)p.H_kv * ((int64_t)C::RB << cp.lg);
+  cp.head_bytes = (int64_t)cp.head * ((int64_t)C::RB << cp.lg);
   cp.pool_records = (int32_t)min((int64_t)cp.blocks * cp.block_bytes, kBufferPoolLimit);
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
@@ -1100,7 +1100,7 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
   if (grid <= 0) return hipSuccess;
   bool flat = flat_gather;
   for (int m = 0; m < 2; ++m)
-    flat |= (int64_t)p.pool_blocks[m] * p.H * ((int64_t)2 * D << p.pool_bs_log2[m]) >
+    flat |= (int64_t)p.pool_blocks[m] * p.H_kv * ((int64_t)2 * D << p.pool_bs_log2[m]) >
             kBufferPoolLimit;
   if (D == 128 && W == 8)
     launch_pp<128>(p, flat, grid, stream);

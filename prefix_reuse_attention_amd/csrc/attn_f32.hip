@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
   const ItemRange x = item_range(p, it);
   const int head = it.h;
+  const int kv_head = head / (p.H / p.H_kv);
   const int tid = threadIdx.x;
   const int rloc = tid / kF32Tpr, part = tid % kF32Tpr;
   const int row = it.m_tile * kF32Rows + rloc;
@@ -62,12 +63,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
         int64_t off;
         const float *kb, *vb;
         if (pre) {
-          off = prefix_offset(p, it.r, x.mode, base + j, head, D);
+          off = prefix_offset(p, it.r, x.mode, base + j, kv_head, D);
           if (off < 0 && p.err) atomicOr(p.err, kErrBlockId);
           kb = (const float *)p.pool_k[x.mode];
           vb = (const float *)p.pool_v[x.mode];
         } else {
-          off = ((int64_t)(x.q0 + base + j) * p.H + head) * D;
+          off = ((int64_t)(x.q0 + base + j) * p.H_kv + kv_head) * D;
           kb = (const float *)p.k;
           vb = (const float *)p.v;
         }

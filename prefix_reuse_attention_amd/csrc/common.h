@@ -52,6 +52,8 @@ struct AttnParams {
   int32_t pool_bs_log2[2];
   int32_t bt_stride;
   int32_t B, H;
+  int32_t H_kv;                   // key/value heads (H for multi-head attention); query
+                                  // head h reads key/value head h / (H / H_kv)
   int32_t total_s;
   float scale_log2;               // softmax_scale * log2(e)
   int32_t chunk_len;              // prefix keys per chunk when split (0 = never)
@@ -104,14 +106,15 @@ __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) 
 }
 
 // Element offset of prefix token `tok` (logical position in the request's
-// prefix) of head h inside its pool, or -1 when the block id is out of range.
+// prefix) of key/value head h inside its pool, or -1 when the block id is out
+// of range.
 __device__ inline int64_t prefix_offset(const AttnParams &p, int r, int mode,
                                         int tok, int h, int D) {
   const int lg = p.pool_bs_log2[mode];
   if ((tok >> lg) >= p.bt_stride) return -1;  // prefix longer than its table row
   const int blk = p.block_table[(int64_t)r * p.bt_stride + (tok >> lg)];
   if (blk < 0 || blk >= p.pool_blocks[mode]) return -1;
-  return (((int64_t)blk * p.H + h) << lg | (tok & ((1 << lg) - 1))) * D;
+  return (((int64_t)blk * p.H_kv + h) << lg | (tok & ((1 << lg) - 1))) * D;
 }
 
 }  // namespace bat

@@ -2,9 +2,10 @@
 // host never waits for the length arrays.
 //
 // Items are (request, head, suffix row tile, prefix chunk).  All tiles of one
-// (request, head, chunk) read the same keys/values, so they form a group that
-// is placed on one XCD (blockIdx % 8 picks the XCD) in consecutive slots, to
-// be served from that XCD's L2.  Groups are ordered longest first (the
+// (request, key/value head, chunk) read the same keys/values -- with grouped
+// heads, the hg query heads of a key/value head too -- so they form a group
+// that is placed on one XCD (blockIdx % 8 picks the XCD) in consecutive
+// slots, to be served from that XCD's L2.  Groups are ordered longest first (the
 // largest per-item key count first) and dealt round-robin over the XCDs, so
 // each XCD's queue also runs longest first, which bounds the tail.
 //
@@ -69,11 +70,12 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 template <typename ReqPtr>
 __device__ __forceinline__ void plan_body(
     const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
-    int32_t B, int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
+    int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
     ReqPtr req, int32_t stride, int32_t (*s_wave)[kNumXcd], int32_t *s_total,
     __attribute__((address_space(3))) int32_t *fast, ReqMeta *__restrict__ meta,
     WorkItem *__restrict__ items, int32_t *hdr) {
   const int tid = threadIdx.x;
+  const int Hk = H / hg;  // key/value heads: groups per request and chunk
   ReqPtr req_key = req, req_order = req + stride, req_ns = req + 2 * stride,
          req_nc = req + 3 * stride;
 
@@ -120,7 +122,7 @@ __device__ __forceinline__ void plan_body(
   int32_t g0[1] = {0}, ng_total[1];
   for (int k = k0; k < k1; ++k) {
     const int r = req_order[k];
-    if (req_ns[r] > 0) g0[0] += H * req_nc[r];
+    if (req_ns[r] > 0) g0[0] += Hk * req_nc[r];
   }
   block_scan<1>(g0, ng_total, s_wave, s_total);
   // 4) slots each XCD gives my groups: group g goes to XCD g % 8
@@ -130,8 +132,8 @@ __device__ __forceinline__ void plan_body(
     const int r = req_order[k];
     const int n_s = req_ns[r];
     if (n_s <= 0) continue;
-    const int T = (n_s + bm - 1) / bm;
-    const int ng = H * req_nc[r];
+    const int T = hg * ((n_s + bm - 1) / bm);  // items per group
+    const int ng = Hk * req_nc[r];
 #pragma unroll
     for (int x = 0; x < kNumXcd; ++x) {
       const int first = g + ((x - g % kNumXcd) + kNumXcd) % kNumXcd;
@@ -141,7 +143,8 @@ __device__ __forceinline__ void plan_body(
     g += ng;
   }
   block_scan<kNumXcd>(slots, used, s_wave, s_total);
-  // 5) write the items (heads fastest within a request's groups, then chunks).
+  // 5) write the items (key/value heads fastest within a request's groups,
+  // then chunks; inside a group, its query heads, each with its row tiles).
   // The j-th group of sorted request k that lands on XCD x takes slots
   // base_k(x) + j*T_k .. +T_k-1 there, base_k(x) being the per-XCD scan above.
   if (B <= kPlanThreads) {
@@ -156,8 +159,8 @@ __device__ __forceinline__ void plan_body(
       r = req_order[tid];
       const int n_s = req_ns[r];
       if (n_s > 0) {
-        T = (n_s + bm - 1) / bm;
-        nit[0] = H * req_nc[r] * T;
+        T = hg * ((n_s + bm - 1) / bm);
+        nit[0] = Hk * req_nc[r] * T;
       }
     }
     block_scan<1>(nit, total, s_wave, s_total);
@@ -183,7 +186,9 @@ __device__ __forceinline__ void plan_body(
       const int x = (G0 + gi) % kNumXcd;
       const int first = ((x - G0 % kNumXcd) + kNumXcd) % kNumXcd;
       const int idx = (s_base[k * kNumXcd + x] + ((gi - first) / kNumXcd) * Tk + t) * kNumXcd + x;
-      if (idx < grid) items[idx] = WorkItem{s_r[k], gi % H, t, gi / H};
+      const int rows = Tk / hg;  // row tiles of each query head
+      if (idx < grid)
+        items[idx] = WorkItem{s_r[k], (gi % Hk) * hg + t / rows, t % rows, gi / Hk};
       else atomicOr(&hdr[kHdrError], kErrLength);  // grid bound too small
     }
   } else {
@@ -192,19 +197,20 @@ __device__ __forceinline__ void plan_body(
     const int r = req_order[k];
     const int n_s = req_ns[r];
     if (n_s <= 0) continue;
-    const int T = (n_s + bm - 1) / bm;
+    const int rows = (n_s + bm - 1) / bm;
+    const int T = hg * rows;
     const int nc = req_nc[r];
-    int h = 0, c = 0;
-    for (int gi = 0; gi < H * nc; ++gi, ++g) {
+    int hk = 0, c = 0;
+    for (int gi = 0; gi < Hk * nc; ++gi, ++g) {
       const int x = g % kNumXcd;
       for (int t = 0; t < T; ++t) {
         const int idx = (slots[x] + t) * kNumXcd + x;
-        if (idx < grid) items[idx] = WorkItem{r, h, t, c};
+        if (idx < grid) items[idx] = WorkItem{r, hk * hg + t / rows, t % rows, c};
         else atomicOr(&hdr[kHdrError], kErrLength);  // grid bound too small
       }
       slots[x] += T;
-      if (++h == H) {
-        h = 0;
+      if (++hk == Hk) {
+        hk = 0;
         ++c;
       }
     }
@@ -220,7 +226,7 @@ __device__ __forceinline__ void plan_body(
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
-    int32_t B, int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
+    int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
     int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
     ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
   __shared__ int32_t s_wave[kPlanWaves][kNumXcd];
@@ -228,19 +234,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ int32_t s_req[4 * kPlanLds];
   __shared__ int32_t s_fast[(kNumXcd + 4) * kPlanThreads];
   if (B <= kPlanLds)
-    plan_body(cu_s, prefix_lens, B, H, bm, chunk_len, max_p, grid, (lds_i32 *)s_req, kPlanLds,
+    plan_body(cu_s, prefix_lens, B, H, hg, bm, chunk_len, max_p, grid, (lds_i32 *)s_req, kPlanLds,
               s_wave, s_total, (lds_i32 *)s_fast, meta, items, hdr);
   else
-    plan_body(cu_s, prefix_lens, B, H, bm, chunk_len, max_p, grid, g_scratch, B, s_wave,
+    plan_body(cu_s, prefix_lens, B, H, hg, bm, chunk_len, max_p, grid, g_scratch, B, s_wave,
               s_total, (lds_i32 *)s_fast, meta, items, hdr);
 }
 
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
-                       int32_t H, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-                       int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
-                       hipStream_t stream) {
+                       int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p,
+                       int32_t grid, int32_t *g_scratch, ReqMeta *meta, WorkItem *items,
+                       int32_t *hdr, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_s, prefix_lens,
-                     B, H, bm, chunk_len, max_p, grid, g_scratch, meta, items, hdr);
+                     B, H, hg, bm, chunk_len, max_p, grid, g_scratch, meta, items, hdr);
   return hipGetLastError();
 }
 

@@ -238,6 +238,34 @@ def test_isolated_workspace_holds_a_partial_per_row(lib):
     assert f(2, 8, 96, api.BAT_BF16, 1024, 512, 1024) == 0
 
 
+def gqa(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, plen=FAKE, mode=FAKE, bt=FAKE, bt_stride=16,
+             up=_pool(), ip=None, B=2, H=8, H_kv=2, D=128, dt=api.BAT_BF16, scale=0.088,
+             total=1024, max_s=512, max_p=1024, out=FAKE, lse=None, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(over)
+    up = ctypes.byref(a["up"]) if a["up"] is not None else None
+    ip = ctypes.byref(a["ip"]) if a["ip"] is not None else None
+    return lib.bat_attn_prefill_gqa(a["q"], a["k"], a["v"], a["cu"], a["plen"], a["mode"],
+                                    a["bt"], a["bt_stride"], up, ip, a["B"], a["H"], a["H_kv"],
+                                    a["D"], a["dt"], a["scale"], a["total"], a["max_s"],
+                                    a["max_p"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(H_kv=3), api.BAT_ERR_INVALID_ARG),           # 8 query heads, 3 key/value heads
+    (dict(H_kv=0), api.BAT_ERR_INVALID_ARG),
+    (dict(H_kv=16), api.BAT_ERR_INVALID_ARG),          # more key/value heads than query heads
+    (dict(k=None), api.BAT_ERR_INVALID_ARG),
+    (dict(D=96), api.BAT_ERR_UNSUPPORTED),
+    (dict(), api.BAT_ERR_WORKSPACE),                   # valid otherwise: no workspace
+    (dict(total=0), api.BAT_OK),
+])
+def test_gqa_argument_errors(lib, over, status):
+    assert gqa(lib, **over) == status
+
+
 def test_lse_merge_argument_errors(lib):
     m = lib.bat_lse_merge
     assert m(FAKE, FAKE, 0, 10, 2, 64, api.BAT_F32, FAKE, None, None) == api.BAT_ERR_INVALID_ARG

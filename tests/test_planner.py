@@ -42,13 +42,14 @@ def _run_plan(wl, monkeypatch):
     return hdr, raw
 
 
-def _check(wl, hdr, raw):
-    B, H = wl.B, wl.H
+def _check(wl, hdr, raw, H=None, hg=1):
+    """H query heads (wl.H by default), hg of them per key/value head."""
+    B, H = wl.B, (wl.H if H is None else H)
     total_s = int(wl.n_s.sum())
     bm = 256 if total_s >= 192 * B else 128
     max_s = int(wl.n_s.max())
     t_max = -(-max_s // bm)
-    grid = 8 * (-(-(H * B) // 8)) * t_max
+    grid = 8 * (-(-((H // hg) * B) // 8)) * hg * t_max
     items = raw[ITEMS_OFF:ITEMS_OFF + 16 * grid].view(np.int32).reshape(grid, 4)
     real = items[items[:, 0] >= 0]
     assert np.all(items[items[:, 0] < 0, 0] == -1), "unused slots must hold request -1"
@@ -72,6 +73,18 @@ def _check(wl, hdr, raw):
         slots = [ts[t] for t in range(len(ts))]
         assert len({s % 8 for s in slots}) == 1, f"group {(r, h)} spans XCDs"
         assert all(b - a == 8 for a, b in zip(slots, slots[1:])), f"group {(r, h)} not consecutive"
+    # with grouped heads: the hg query heads of one key/value head follow one
+    # another on one XCD, head by head
+    if hg > 1:
+        for r in range(B):
+            for hk in range(H // hg):
+                seq = [pos[(r, h)][t] for h in range(hk * hg, (hk + 1) * hg)
+                       if (r, h) in pos for t in range(len(pos[(r, h)]))]
+                if not seq:
+                    continue
+                assert len({s % 8 for s in seq}) == 1, f"kv group {(r, hk)} spans XCDs"
+                assert all(b - a == 8 for a, b in zip(seq, seq[1:])), \
+                    f"kv group {(r, hk)} not consecutive"
     # longest first on every XCD
     key = wl.n_s.astype(np.int64) + np.minimum(wl.n_p, int(wl.n_p.max())).astype(np.int64)
     for x in range(8):
@@ -91,3 +104,32 @@ def test_plan_items(gpu_ready, monkeypatch, B, seed):
     print(f"[planner] B={B} total_s={int(n_s.sum())}", flush=True)
     hdr, raw = _run_plan(wl, monkeypatch)
     _check(wl, hdr, raw)
+
+
+@pytest.mark.parametrize("B,hg,seed", [(16, 4, 6), (300, 2, 7)])
+def test_plan_items_grouped_heads(gpu_ready, monkeypatch, B, hg, seed):
+    """Grouped key/value heads (8 query heads over 8 / hg key/value heads),
+    through bat_attn_prefill_gqa; both planner paths."""
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_device
+    monkeypatch.setenv("BAT_SPLIT_CHUNK", "1000000")
+    rng = np.random.default_rng(2000 + seed)
+    n_s = rng.integers(1, 600, size=B)
+    n_s[rng.random(B) < 0.1] = 0
+    n_p = rng.integers(0, 700, size=B)
+    H = 8
+    wl = W.make_custom(dtype="bf16", H=H // hg, D=64, n_s=n_s.tolist(), n_p=n_p.tolist(),
+                       mode=[W.USER] * B, seed=seed, user_block_size=64,
+                       name=f"plan_gqa_B{B}")
+    print(f"[planner] gqa B={B} hg={hg} total_s={int(n_s.sum())}", flush=True)
+    dw = DeviceWorkload(wl)
+    q = to_device(W._normal(rng, (wl.total_s, H, wl.D), "bf16"), "bf16")
+    n = api.load().bat_attn_gqa_workspace_size(B, H, H // hg, wl.D, api.BAT_BF16, wl.total_s,
+                                               dw.max_s, dw.max_p)
+    ws = torch.full((max(int(n), 1),), 0xAB, dtype=torch.uint8, device="cuda")
+    api.attn_prefill_gqa(q, dw.k, dw.v, dw.cu_s, dw.prefix_lens, dw.prefix_mode, dw.block_table,
+                         dw.user_pool, dw.item_pool, wl.scale, dw.max_s, dw.max_p, workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    _check(wl, raw[:HDR_BYTES].view(np.int32), raw, H=H, hg=hg)

@@ -237,3 +237,86 @@ def make_config(k: int, seed=None, materialize=True) -> Workload:
         raise ValueError(f"unknown configuration {k}")
     wl.notes["description"] = CONFIG_DESCRIPTIONS[k]
     return wl
+
+
+@dataclass
+class Traffic:
+    """A seeded stream of generative-recommender queries: query r comes from
+    user `user[r]` (history of `user_len[user[r]]` tokens) and scores the
+    `items.shape[1]` distinct candidate items `items[r]` of ITEM_TOKENS tokens
+    each."""
+    seed: int
+    user: np.ndarray       # [R] int32 user ids
+    user_len: np.ndarray   # [num_users] int32 history tokens per user
+    items: np.ndarray      # [R, m] int32 item ids, distinct within a row
+    num_items: int
+    item_tokens: int = ITEM_TOKENS
+
+    @property
+    def num_users(self) -> int:
+        return len(self.user_len)
+
+    @property
+    def R(self) -> int:
+        return len(self.user)
+
+
+def _zipf_ranks(rng, n, s, size):
+    """`size` ranks (0-based) with p(rank k) ~ (k+1)^-s, with replacement."""
+    cdf = np.cumsum(np.arange(1, n + 1, dtype=np.float64) ** (-s))
+    cdf /= cdf[-1]
+    return np.minimum(np.searchsorted(cdf, rng.random(size), side="right"), n - 1)
+
+
+def make_traffic(seed, n_requests, num_users, num_items=NUM_ITEMS, items_per_request=128,
+                 user_len_range=(256, 4096), user_len_step=64, user_zipf_s=0.9,
+                 item_zipf_s=ZIPF_S):
+    """Synthetic Zipf traffic for the prefix-mode choice.
+
+    Users recur with Zipf(user_zipf_s) popularity; each user's history length
+    is fixed, a multiple of user_len_step drawn uniformly from user_len_range.
+    Each query's items are Zipf(item_zipf_s) draws without replacement (the
+    first items_per_request distinct ids of a stream of independent draws,
+    which is successive weighted sampling without replacement).  Ranks map to
+    ids through seeded permutations so hot users and items are spread over
+    the id space.
+    """
+    rng = np.random.default_rng(seed)
+    lo, hi = user_len_range
+    user_len = (rng.integers(lo // user_len_step, hi // user_len_step, endpoint=True,
+                             size=num_users) * user_len_step).astype(np.int32)
+    user_perm = rng.permutation(num_users).astype(np.int32)
+    user = user_perm[_zipf_ranks(rng, num_users, user_zipf_s, n_requests)]
+    item_perm = rng.permutation(num_items).astype(np.int32)
+    m = int(items_per_request)
+    if m > num_items:
+        raise ValueError("more items per request than the pool has")
+    items = np.empty((n_requests, m), np.int32)
+    K = 4 * m + 16  # draws per query; a query short of m distinct ids draws more
+    for r0 in range(0, n_requests, 4096):
+        r1 = min(n_requests, r0 + 4096)
+        draws = _zipf_ranks(rng, num_items, item_zipf_s, (r1 - r0, K))
+        # first occurrence of each id in its row's draw order
+        order = np.argsort(draws, axis=1, kind="stable")
+        srt = np.take_along_axis(draws, order, axis=1)
+        first_sorted = np.ones_like(srt, dtype=bool)
+        first_sorted[:, 1:] = srt[:, 1:] != srt[:, :-1]
+        first = np.zeros_like(first_sorted)
+        np.put_along_axis(first, order, first_sorted, axis=1)
+        take = first & (np.cumsum(first, axis=1) <= m)
+        full = take.sum(axis=1) == m
+        items[r0:r1][full] = item_perm[draws[full][take[full]].reshape(-1, m)]
+        for i in np.nonzero(~full)[0]:
+            got = [int(x) for x in draws[i][take[i]]]
+            seen = set(got)
+            while len(got) < m:
+                for k in _zipf_ranks(rng, num_items, item_zipf_s, 2 * (m - len(got)) + 8):
+                    k = int(k)
+                    if k not in seen:
+                        seen.add(k)
+                        got.append(k)
+                        if len(got) == m:
+                            break
+            items[r0 + i] = item_perm[np.asarray(got)]
+    return Traffic(seed=seed, user=user.astype(np.int32), user_len=user_len, items=items,
+                   num_items=num_items)

@@ -336,6 +336,93 @@ bat_status bat_lse_merge(const float *o_parts, const float *lse_parts,
                          int32_t n_parts, int32_t rows, int32_t H, int32_t D,
                          bat_dtype dt, void *out, float *lse, void *stream);
 
+/*
+ * Prefix-mode choice (host side).
+ *
+ * The Bat page (sections "The idea" and "Why it works") has a hotness-aware
+ * scheduler pick, per query and under memory limits, the user history or the
+ * query's items as the cached prefix, favouring caches that are hot and
+ * resident; user-prefix and item-prefix caches live in separate pools.  The
+ * page gives no policy in detail.  These calls implement one plain reading,
+ * query by query in arrival order:
+ *   score  user mode: n_u (user resident), else n_u * requests_u when the
+ *          user's blocks fit the user pool, else 0;
+ *          item mode: T * sum over the query's m items of 1 (resident) or
+ *          requests_i (missing, when the item pool has slots).
+ *          Item mode only on a strictly larger score (BAT_POLICY_HOTNESS);
+ *          BAT_POLICY_USER_PREFIX always picks the user (the conventional
+ *          baseline).  requests_x counts the earlier queries naming x.
+ *   cache  only the chosen prefix: the user pool evicts least recently used
+ *          users until ceil(n_u / user_block) blocks fit (a user larger
+ *          than the pool is never kept); each missing item takes the lowest
+ *          unused slot, else replaces the resident item, not of this query,
+ *          with the fewest requests, then least recent use, then lowest id,
+ *          if that item had strictly fewer requests than the newcomer.
+ *   count  the user and every item of the query gain one request.
+ *   work   user mode: prefix tokens computed = 0 on a hit else n_u, suffix
+ *          tokens = m*T, query-key pairs = (0 or n_u^2) + m*T*(n_u + m*T);
+ *          item mode: prefix = T*(m - hits), suffix = n_u,
+ *          pairs = (m - hits)*T^2 + n_u*(n_u + m*T).
+ * All state lives in a caller-owned host buffer (no allocation, no hidden
+ * state); one buffer serves one stream of queries, calls on the same buffer
+ * must not overlap.
+ */
+typedef enum bat_sched_policy {
+  BAT_POLICY_USER_PREFIX = 0, /* always the user history (baseline) */
+  BAT_POLICY_HOTNESS = 1      /* the scoring above */
+} bat_sched_policy;
+
+typedef struct bat_sched_config {
+  int32_t policy;               /* bat_sched_policy */
+  int32_t item_tokens;          /* T > 0, tokens per item */
+  int32_t user_block;           /* > 0, tokens per user-pool block */
+  int32_t item_capacity;        /* >= 0, item-pool slots */
+  int64_t user_capacity_blocks; /* >= 0, user-pool blocks */
+  int32_t num_users;            /* >= 0, user ids are 0 .. num_users-1 */
+  int32_t num_items;            /* >= 0, item ids are 0 .. num_items-1 */
+} bat_sched_config;
+
+/* Bytes of host state for cfg; 0 if cfg is NULL or invalid. */
+size_t bat_sched_state_size(const bat_sched_config *cfg);
+
+/*
+ * bat_sched_init -- empty pools, zero request counts.
+ *   user_len  host int32 [num_users], history tokens per user (>= 0)
+ *   state     host buffer, 8-byte aligned, >= bat_sched_state_size(cfg)
+ *             bytes, owned by the caller (BAT_ERR_WORKSPACE if smaller)
+ */
+bat_status bat_sched_init(const bat_sched_config *cfg, const int32_t *user_len,
+                          void *state, size_t state_bytes);
+
+/*
+ * bat_sched_step -- serve R queries of m items each, in order; the state
+ * carries over between calls (the query clock continues).
+ *   user      host int32 [R], ids < num_users
+ *   items     host int32 [R, m], ids < num_items, distinct within a query
+ *   outputs   host arrays, each may be NULL:
+ *             mode [R] uint8 (bat_prefix_mode), user_hit [R] uint8,
+ *             item_hits [R] int32 (the query's resident items when it
+ *             arrived, whatever the mode), prefix_tokens / suffix_tokens /
+ *             pairs [R] int64 (the work above), item_slot [R, m] int32
+ *             (item mode: the slot each item is read from or was stored
+ *             in; -1 for an item not kept and for every user-mode query).
+ * Any out-of-range id or repeated item returns BAT_ERR_INVALID_ARG before
+ * any query is served.
+ */
+bat_status bat_sched_step(void *state, int32_t R, int32_t m, const int32_t *user,
+                          const int32_t *items, uint8_t *mode, uint8_t *user_hit,
+                          int32_t *item_hits, int64_t *prefix_tokens,
+                          int64_t *suffix_tokens, int64_t *pairs,
+                          int32_t *item_slot);
+
+/*
+ * bat_sched_pools -- the pools' contents: resident users, most recently
+ * used first (host int32 [num_users] or NULL), their number, and the item
+ * in each item-pool slot (host int32 [item_capacity] or NULL; -1 unused).
+ */
+bat_status bat_sched_pools(const void *state, int32_t *resident_users,
+                           int32_t *n_resident_users, int32_t *slot_item);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *bat_status_string(bat_status s);
 

@@ -20,8 +20,10 @@ BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill",
             "bat_attn_prefix_rows", "bat_attn_item_local", "bat_attn_isolated_workspace_size",
             "bat_attn_prefill_isolated", "bat_attn_gqa_workspace_size", "bat_attn_prefill_gqa",
-            "bat_lse_merge",
+            "bat_lse_merge", "bat_sched_state_size", "bat_sched_init", "bat_sched_step",
+            "bat_sched_pools",
             "bat_status_string", "bat_version")
+BAT_POLICY_USER_PREFIX, BAT_POLICY_HOTNESS = 0, 1
 
 _lib = None
 
@@ -30,6 +32,13 @@ class BatError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
         super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class SchedConfig(ctypes.Structure):
+    _fields_ = [("policy", ctypes.c_int32), ("item_tokens", ctypes.c_int32),
+                ("user_block", ctypes.c_int32), ("item_capacity", ctypes.c_int32),
+                ("user_capacity_blocks", ctypes.c_int64), ("num_users", ctypes.c_int32),
+                ("num_items", ctypes.c_int32)]
 
 
 class KvPool(ctypes.Structure):
@@ -72,6 +81,15 @@ def load():
     lib.bat_attn_prefill_gqa.restype = I
     lib.bat_lse_merge.argtypes = [P, P, I, I, I, I, I, P, P, P]
     lib.bat_lse_merge.restype = I
+    SP = ctypes.POINTER(SchedConfig)
+    lib.bat_sched_state_size.argtypes = [SP]
+    lib.bat_sched_state_size.restype = ctypes.c_size_t
+    lib.bat_sched_init.argtypes = [SP, P, P, ctypes.c_size_t]
+    lib.bat_sched_init.restype = I
+    lib.bat_sched_step.argtypes = [P, I, I, P, P, P, P, P, P, P, P, P]
+    lib.bat_sched_step.restype = I
+    lib.bat_sched_pools.argtypes = [P, P, P, P]
+    lib.bat_sched_pools.restype = I
     lib.bat_status_string.argtypes = [I]
     lib.bat_status_string.restype = ctypes.c_char_p
     lib.bat_version.argtypes = []
@@ -392,3 +410,55 @@ def lse_merge(o_parts, lse_parts, out_dtype, out=None, lse=None, want_lse=True):
                               _dtype_code(out), _ptr(out), _ptr(lse), _stream())
     _check(st, "bat_lse_merge")
     return out, lse
+
+
+class Scheduler:
+    """The library's prefix-mode choice over a stream of queries (host side).
+
+    Holds the caller-owned state buffer bat_sched_* works in; numpy arrays
+    in and out (the choice runs on the host, not on the GPU)."""
+
+    def __init__(self, policy, item_tokens, user_block, user_capacity_blocks, item_capacity,
+                 user_len, num_items):
+        import numpy as np
+        self._np = np
+        self.user_len = np.ascontiguousarray(user_len, dtype=np.int32)
+        self.cfg = SchedConfig(int(policy), int(item_tokens), int(user_block),
+                               int(item_capacity), int(user_capacity_blocks),
+                               len(self.user_len), int(num_items))
+        lib = load()
+        n = int(lib.bat_sched_state_size(ctypes.byref(self.cfg)))
+        if n == 0:
+            raise BatError(BAT_ERR_INVALID_ARG, "bat_sched_state_size")
+        self.state = np.zeros((n + 7) // 8, dtype=np.int64)  # 8-byte aligned
+        _check(lib.bat_sched_init(ctypes.byref(self.cfg), self.user_len.ctypes.data,
+                                  self.state.ctypes.data, self.state.nbytes), "bat_sched_init")
+
+    def step(self, user, items):
+        """Serve queries in order; returns a dict of per-query arrays."""
+        np = self._np
+        user = np.ascontiguousarray(user, dtype=np.int32)
+        items = np.ascontiguousarray(items, dtype=np.int32)
+        R, m = items.shape
+        if user.shape != (R,):
+            raise BatError(BAT_ERR_INVALID_ARG, "Scheduler.step: user and items disagree")
+        out = {"mode": np.empty(R, np.uint8), "user_hit": np.empty(R, np.uint8),
+               "item_hits": np.empty(R, np.int32), "prefix_tokens": np.empty(R, np.int64),
+               "suffix_tokens": np.empty(R, np.int64), "pairs": np.empty(R, np.int64),
+               "item_slot": np.empty((R, m), np.int32)}
+        _check(load().bat_sched_step(
+            self.state.ctypes.data, R, m, user.ctypes.data, items.ctypes.data,
+            *(out[k].ctypes.data for k in ("mode", "user_hit", "item_hits", "prefix_tokens",
+                                           "suffix_tokens", "pairs", "item_slot"))),
+            "bat_sched_step")
+        return out
+
+    def pools(self):
+        """(resident users, most recent first; item in each slot, -1 unused)."""
+        np = self._np
+        users = np.empty(max(len(self.user_len), 1), np.int32)
+        n = ctypes.c_int32(0)
+        slots = np.empty(max(self.cfg.item_capacity, 1), np.int32)
+        _check(load().bat_sched_pools(self.state.ctypes.data, users.ctypes.data,
+                                      ctypes.addressof(n), slots.ctypes.data), "bat_sched_pools")
+        return users[:n.value].copy(), slots[:self.cfg.item_capacity].copy()

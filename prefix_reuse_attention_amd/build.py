@@ -2,7 +2,7 @@
 
     python -m prefix_reuse_attention_amd.build [-v]
 
-Each csrc/*.hip compiles to an object under _build/ (in parallel), then they
+Each csrc/*.hip (and the host-only csrc/*.cpp) compiles to an object under _build/ (in parallel), then they
 link into prefix_reuse_attention_amd/libbat.so.  Every HIP source is compiled
 with packed-fp32 instructions disabled (-packed-fp32-ops).
 """
@@ -51,7 +51,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]

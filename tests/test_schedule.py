@@ -200,3 +200,99 @@ def test_oracle_admission_needs_strictly_fewer_requests():
     assert res["item_slot"][:, 0].tolist() == [-1, -1, 0, -1, -1, 0]
     assert res["item_hits"].tolist() == [0, 0, 0, 0, 0, 0]
     assert res["slot_item"].tolist() == [1]
+
+
+# ---- the library's scheduler against the oracle ------------------------
+
+def _native(tr_user, user_len, items, T, block, ucap, icap, policy, num_items, chunks=(1,)):
+    from prefix_reuse_attention_amd import api
+    sch = api.Scheduler(policy, T, block, ucap, icap, user_len, num_items)
+    R = len(tr_user)
+    parts, at = [], 0
+    cuts = sorted({0, R, *[int(R * c) for c in chunks]})
+    for a, b in zip(cuts, cuts[1:]):
+        parts.append(sch.step(tr_user[a:b], items[a:b]))
+    res = {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    res["resident_users"], res["slot_item"] = sch.pools()
+    return res
+
+
+KEYS = ("mode", "user_hit", "item_hits", "prefix_tokens", "suffix_tokens", "pairs",
+        "item_slot", "resident_users", "slot_item")
+
+
+def _same(a, b):
+    for k in KEYS:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
+@pytest.mark.parametrize("policy", [S.POLICY_HOTNESS, S.POLICY_USER_PREFIX])
+def test_native_hand_trace(policy):
+    g = _golden()
+    ref = _run_oracle(g, policy)
+    got = _native(np.asarray(g["user"], np.int32), g["user_len"],
+                  np.asarray(g["items"], np.int32), g["item_tokens"], g["user_block"],
+                  g["user_capacity_blocks"], g["item_capacity"], policy, g["num_items"],
+                  chunks=(0.5,))
+    _same(got, ref)
+
+
+@pytest.mark.parametrize("seed,ucap,icap,policy", [
+    (20, 0, 0, 1), (21, 10, 0, 1), (22, 30, 16, 1), (23, 60, 60, 1), (24, 200, 1, 1),
+    (25, 30, 16, 0), (26, 12, 40, 1), (27, 10 ** 9, 10 ** 4, 1)])
+def test_native_matches_oracle(seed, ucap, icap, policy):
+    tr = _small_traffic(seed, R=600, users=50, items=120, m=9)
+    ref = S.schedule(tr.user, tr.user_len, tr.items, 4, 64, ucap, icap, policy,
+                     num_items=tr.num_items)
+    got = _native(tr.user, tr.user_len, tr.items, 4, 64, ucap, icap, policy, tr.num_items,
+                  chunks=(0.13, 0.5, 0.51))
+    _same(got, ref)
+    if policy == S.POLICY_HOTNESS and 0 < icap < 10 ** 4:
+        assert 0 < got["mode"].sum() < tr.R
+
+
+def test_native_zipf_traffic_against_oracle():
+    """Traffic shaped like the measured one (Zipf users and items, 64-token
+    user blocks, 4-token items), sized for the oracle."""
+    tr = W.make_traffic(28, 2000, 400, num_items=2000, items_per_request=32,
+                        user_len_range=(256, 4096))
+    ref = S.schedule(tr.user, tr.user_len, tr.items, 4, 64, 2000, 300, S.POLICY_HOTNESS,
+                     num_items=tr.num_items)
+    got = _native(tr.user, tr.user_len, tr.items, 4, 64, 2000, 300, S.POLICY_HOTNESS,
+                  tr.num_items, chunks=(0.25, 0.75))
+    _same(got, ref)
+
+
+def test_native_rejects_bad_queries():
+    from prefix_reuse_attention_amd import api
+    sch = api.Scheduler(1, 4, 64, 10, 4, [100, 200], 10)
+    for user, items in (([0, 2], [[1, 2], [3, 4]]),      # user id out of range
+                        ([0, 1], [[1, 2], [3, 10]]),     # item id out of range
+                        ([0, 1], [[1, 2], [3, 3]]),      # repeated item
+                        ([0, -1], [[1, 2], [3, 4]])):
+        with pytest.raises(api.BatError):
+            sch.step(np.asarray(user), np.asarray(items))
+    # the argument check stamps items but serves no query
+    got = sch.step(np.asarray([0]), np.asarray([[1, 2]]))
+    assert got["mode"].tolist() == [0] and got["user_hit"].tolist() == [0]
+    with pytest.raises(api.BatError):
+        api.Scheduler(7, 4, 64, 10, 4, [100], 10)       # unknown policy
+    with pytest.raises(api.BatError):
+        api.Scheduler(1, 0, 64, 10, 4, [100], 10)       # T = 0
+
+
+def test_native_matches_oracle_under_eviction_pressure():
+    """Small pools against many users and items: user evictions, item
+    replacements and rejected admissions all happen (checked), T = 2."""
+    tr = W.make_traffic(29, 1500, 80, num_items=150, items_per_request=12,
+                        user_len_range=(64, 1024), user_zipf_s=0.6, item_zipf_s=0.8)
+    args = (tr.user, tr.user_len, tr.items, 2, 64, 20, 24, S.POLICY_HOTNESS)
+    ref = S.schedule(*args, num_items=tr.num_items)
+    got = _native(*args, tr.num_items, chunks=(0.3, 0.6))
+    _same(got, ref)
+    item_q = got["mode"] == S.MODE_ITEM
+    missing = tr.items.shape[1] - got["item_hits"][item_q]
+    kept = (got["item_slot"][item_q] >= 0).sum(axis=1) - got["item_hits"][item_q]
+    assert (kept > 0).any() and (kept < missing).any(), "no admissions or no rejections"
+    ever = set(tr.user[(got["mode"] == S.MODE_USER) & (got["user_hit"] == 0)].tolist())
+    assert len(got["resident_users"]) < len(ever), "no user evictions"

@@ -13,14 +13,13 @@ arrive:
 
 1. Reuse now.  The user's cache is resident or not (user pool); each of the
    query's m items is resident or not (item pool).
-2. Choice.  Each mode scores the prefix tokens it reuses now plus the prefix
-   tokens it would make resident weighted by how often they were asked for
-   before (their hotness: the number of earlier queries naming them):
-       user mode: n_u if the user is resident, else n_u * count_u when the
-                  user's blocks fit in the user pool at all, else 0;
-       item mode: T * sum over the query's items of (1 if resident, else
-                  count_i), 0 for a missing item when the item pool has no
-                  slots.
+2. Choice.  Each mode scores the prefix tokens that are hot: resident now,
+   or asked for by an earlier query (hotness: the number of earlier queries
+   naming them is above zero) and able to stay resident:
+       user mode: n_u if the user is resident, or if it was asked for before
+                  and its blocks fit in the user pool at all; else 0;
+       item mode: T for each of the query's items that is resident, or was
+                  asked for before while the item pool has slots.
    Item mode is chosen when its score is larger; a tie keeps the user as
    the prefix (the conventional choice).  The user-as-prefix policy always
    chooses user mode.
@@ -99,18 +98,12 @@ def schedule(user, user_len, items, item_tokens, user_block, user_capacity_block
         if policy == POLICY_USER_PREFIX:
             mode = MODE_USER
         else:
-            if u_hit:
-                s_user = n_u
-            elif blocks(n_u) <= user_capacity_blocks:
-                s_user = n_u * count_u[u]
-            else:
-                s_user = 0
+            hot_user = u_hit or (count_u[u] > 0 and blocks(n_u) <= user_capacity_blocks)
+            s_user = n_u if hot_user else 0
             s_item = 0
             for i, res in zip(its, resident):
-                if res:
+                if res or (count_i[i] > 0 and item_capacity > 0):
                     s_item += T
-                elif item_capacity > 0:
-                    s_item += T * count_i[i]
             mode = MODE_ITEM if s_item > s_user else MODE_USER
         # 3) cache update and accounting
         if mode == MODE_USER:

@@ -101,13 +101,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--workload", choices=("prefill", "isolated", "gqa", "prefix-rows",
-                                           "item-local"),
+                                           "item-local", "schedule"),
                     default="prefill",
                     help="prefill: bat_attn_prefill on --config (the default line); "
                          "isolated: bat_attn_prefill_isolated on --config with single-token "
                          "candidates; gqa: bat_attn_prefill_gqa on the 8k-history shape with 4 "
                          "key/value heads for its 16 query heads; prefix-rows: bat_attn_prefix_rows over the 8k-history "
-                         "prefixes; item-local: bat_attn_item_local over the 20000-item pool")
+                         "prefixes; item-local: bat_attn_item_local over the 20000-item pool; "
+                         "schedule: the prefix-mode choice (bat_sched_*) on Zipf traffic and "
+                         "the attention work it implies for a window of queries")
+    ap.add_argument("--host-sweep", action="store_true",
+                    help="with --workload schedule: only the host accounting of both policies "
+                         "over a grid of traffic shapes (no GPU needed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -143,9 +148,15 @@ def main():
     from prefix_reuse_attention_amd.device import DeviceWorkload
 
     api.load()  # the HIP library must be there: no fallback
+    if args.workload == "schedule" and args.host_sweep:
+        schedule_host_sweep()  # host code only
+        return
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "schedule":
+        bench_schedule_workload(args)
+        return
     if args.workload in ("prefix-rows", "item-local"):
         bench_prefix_workload(args)
         return
@@ -436,6 +447,205 @@ def bench_prefix_workload(args):
         line["cpu_baseline"] = _prefix_cpu_baseline(args.workload, rng, H, D, scale,
                                                     n_p if args.workload == "prefix-rows" else T,
                                                     args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+SCHED = dict(n_requests=40000, num_users=20000, num_items=20000, items_per_request=128,
+             user_len_range=(256, 4096), user_zipf_s=0.9, item_zipf_s=1.1, seed=7,
+             budget_tokens=1 << 21, item_slots=8192, user_block=64, window=64, H=8, D=128)
+
+
+def _window_work(tr, res, lo, hi, H, D, seed):
+    """The attention work a policy's choices imply for queries lo..hi-1, on
+    the device: the prefill of every query over its prefix (user mode: the
+    m*T item tokens over the user history; item mode: the user tokens over
+    the query's items), prefix rows of the users it missed and per-item rows
+    of the items it missed.  Returns a step callable and its query-key pairs."""
+    import numpy as np
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd import workloads as W
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_device
+    T, m = tr.item_tokens, tr.items.shape[1]
+    n_u = tr.user_len[tr.user[lo:hi]].astype(np.int32)
+    mode = res["mode"][lo:hi].astype(np.uint8)
+    item = mode == W.ITEM
+    n_s = np.where(item, n_u, m * T).astype(np.int32)
+    n_p = np.where(item, m * T, n_u).astype(np.int32)
+    wl = W.make_custom(dtype="bf16", H=H, D=D, n_s=n_s, n_p=n_p, mode=mode, seed=seed,
+                       num_items=tr.num_items, name="schedule window")
+    for r in np.nonzero(item)[0]:           # the queries' own items
+        wl.block_table[r, :m] = tr.items[lo + r]
+    dw = DeviceWorkload(wl)
+    ws = dw.workspace()
+    out = torch.empty_like(dw.q)
+    rng = np.random.default_rng(seed + 1)
+    miss_u = (~item) & (res["user_hit"][lo:hi] == 0)
+    lens = n_u[miss_u]
+    pr = None
+    if len(lens):
+        n = int(lens.sum())
+        pq, pk, pv = (to_device(W._normal(rng, (n, H, D), "bf16"), "bf16") for _ in range(3))
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
+        pws = torch.empty(max(1, api.workspace_size(len(lens), H, D, api.BAT_BF16, n,
+                                                    int(lens.max()), 0)),
+                          dtype=torch.uint8, device="cuda")
+        pout = torch.empty_like(pq)
+        pr = lambda: api.attn_prefix_rows(pq, pk, pv, cu, softmax_scale=wl.scale,
+                                          max_prefix_len=int(lens.max()), out=pout, workspace=pws)
+    n_miss_items = int((m - res["item_hits"][lo:hi])[item].sum())
+    il = None
+    if n_miss_items:
+        iq, ik, iv = (to_device(W._normal(rng, (n_miss_items * T, H, D), "bf16"), "bf16")
+                      for _ in range(3))
+        iout = torch.empty_like(iq)
+        il = lambda: api.attn_item_local(iq, ik, iv, T, softmax_scale=wl.scale, out=iout)
+
+    def step():
+        if pr is not None:
+            pr()
+        if il is not None:
+            il()
+        dw.run(out=out, workspace=ws, want_lse=False)
+    return step, int(res["pairs"][lo:hi].sum())
+
+
+def _policy_accounting(tr, c):
+    """Both policies over the whole stream with the library's scheduler:
+    per-policy results and summary."""
+    from prefix_reuse_attention_amd import api
+    T, m, bs, budget = tr.item_tokens, tr.items.shape[1], c["user_block"], c["budget_tokens"]
+    pol = {"user_prefix": (api.BAT_POLICY_USER_PREFIX, budget // bs, 0),
+           "hotness": (api.BAT_POLICY_HOTNESS, (budget - c["item_slots"] * T) // bs,
+                       c["item_slots"])}
+    res, host = {}, {}
+    for name, (p, ucap, icap) in pol.items():
+        sch = api.Scheduler(p, T, bs, ucap, icap, tr.user_len, tr.num_items)
+        t = time.perf_counter()
+        res[name] = sch.step(tr.user, tr.items)
+        dt = time.perf_counter() - t
+        r = res[name]
+        host[name] = {
+            "user_capacity_blocks": int(ucap), "item_slots": int(icap),
+            "item_mode_frac": round(float(r["mode"].mean()), 4),
+            "user_hit_frac": round(float(r["user_hit"][r["mode"] == 0].mean()), 4),
+            "item_hit_frac": round(float(r["item_hits"][r["mode"] == 1].sum()
+                                         / max(1, m * (r["mode"] == 1).sum())), 4),
+            "computed_tokens": int(r["prefix_tokens"].sum() + r["suffix_tokens"].sum()),
+            "pairs": int(r["pairs"].sum()),
+            "scheduler_queries_per_s": round(tr.R / dt, 1)}
+    b, h = host["user_prefix"], host["hotness"]
+    accounting = {
+        "computed_tokens_vs_user_prefix": round(h["computed_tokens"] / b["computed_tokens"], 4),
+        "pairs_vs_user_prefix": round(h["pairs"] / b["pairs"], 4)}
+    return pol, res, host, accounting
+
+
+def _traffic(c):
+    from prefix_reuse_attention_amd import workloads as W
+    return W.make_traffic(c["seed"], c["n_requests"], c["num_users"], num_items=c["num_items"],
+                          items_per_request=c["items_per_request"],
+                          user_len_range=c["user_len_range"], user_zipf_s=c["user_zipf_s"],
+                          item_zipf_s=c["item_zipf_s"])
+
+
+def schedule_host_sweep():
+    """Host accounting of both policies over traffic shapes around the
+    measured one (20000 queries each): user history range, items per query,
+    user popularity skew.  One JSON line per shape."""
+    for lens in ((256, 1024), (256, 4096), (1024, 8192)):
+        for m in (64, 128, 512):
+            for uz in (0.6, 0.9, 1.2):
+                c = dict(SCHED, n_requests=20000, user_len_range=lens, items_per_request=m,
+                         user_zipf_s=uz)
+                tr = _traffic(c)
+                _, _, host, acc = _policy_accounting(tr, c)
+                print(json.dumps({"user_len_range": list(lens), "items_per_request": m,
+                                  "user_zipf_s": uz,
+                                  "item_mode_frac": host["hotness"]["item_mode_frac"],
+                                  "user_hit_frac_user_prefix": host["user_prefix"]["user_hit_frac"],
+                                  **acc}), flush=True)
+
+
+def bench_schedule_workload(args):
+    """The prefix-mode choice on seeded Zipf traffic.
+
+    Host: the library's scheduler (bat_sched_*) serves the whole stream under
+    the user-as-prefix policy (every token of the cache budget for users) and
+    the hotness-aware one (the same budget less `item_slots` items of T
+    tokens for the item pool); the accounting of both.  Device: a window of
+    consecutive queries at the end of the stream (warm pools), with the
+    attention work each policy's choices imply run through the library's
+    kernels, timed per window.  One JSON line; `value` is queries per second
+    of the hotness-aware window's attention work."""
+    import numpy as np
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd import workloads as W
+    c = SCHED
+    t = time.perf_counter()
+    tr = _traffic(c)
+    T, m, bs = tr.item_tokens, tr.items.shape[1], c["user_block"]
+    budget = c["budget_tokens"]
+    print(f"[bench] traffic: {tr.R} queries, {tr.num_users} users, {tr.num_items} items, "
+          f"generated in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
+    pol, res, host, accounting = _policy_accounting(tr, c)
+    print(f"[bench] host: {json.dumps(host)} {json.dumps(accounting)}", file=sys.stderr,
+          flush=True)
+
+    H, D, B = c["H"], c["D"], c["window"]
+    lo, hi = tr.R - B, tr.R
+    stream = torch.cuda.current_stream()
+    steps, warmup = max(1, min(args.steps, 50)), max(1, min(args.warmup, 10))
+    dev = {}
+    for name in pol:
+        step, pairs = _window_work(tr, res[name], lo, hi, H, D, seed=c["seed"] + 10)
+        wall_ms, kernel_ms = _timed_steps(step, steps, warmup, stream)
+        dev[name] = {"ms_per_window": round(kernel_ms, 5), "wall_ms": round(wall_ms, 5),
+                     "pairs": pairs, "item_mode_queries": int(res[name]["mode"][lo:hi].sum())}
+        print(f"[bench] window {name}: {kernel_ms:.4f} ms (events), {wall_ms:.4f} ms wall, "
+              f"{pairs} pairs", file=sys.stderr, flush=True)
+        del step
+        torch.cuda.empty_cache()
+    hk = dev["hotness"]
+    flops = 4.0 * D * H * hk["pairs"]
+    achieved = flops / (hk["ms_per_window"] * 1e-3) / 1e12
+    line = {"workload": "schedule", "metric": "queries/s of the attention work a window of "
+            "queries needs under the hotness-aware prefix choice, 1 GPU",
+            "value": round(B / (hk["wall_ms"] * 1e-3), 1), "unit": "queries/s",
+            "higher_is_better": True, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": hk["wall_ms"], "dtype": "bf16",
+            "data": "synthetic (seeded Zipf traffic, N(0,1) activations)",
+            "config": {"workload": f"prefix-mode choice: {tr.R} queries, {tr.num_users} users "
+                       f"Zipf({c['user_zipf_s']}) with U{list(c['user_len_range'])} tokens, "
+                       f"{m} of {tr.num_items} items Zipf({c['item_zipf_s']}) x {T} tokens, "
+                       f"cache budget {budget} tokens; window of the last {B} queries, "
+                       f"H={H}, D={D}, bf16", **{k: v for k, v in c.items()}},
+            "vs_baseline": None,
+            "speedup_vs_user_prefix": round(dev["user_prefix"]["ms_per_window"]
+                                            / hk["ms_per_window"], 4),
+            "host": host, "accounting": accounting, "device": dev,
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel": "window: prefix rows + per-item rows + prefill",
+                         "kernel_ms_mean": hk["ms_per_window"]}}
+    if not args.no_cpu_baseline:
+        import oracle.schedule as OS
+        n = 2000
+        while True:
+            t = time.perf_counter()
+            p, ucap, icap = pol["hotness"]
+            OS.schedule(tr.user[:n], tr.user_len, tr.items[:n], T, bs, ucap, icap, p,
+                        num_items=tr.num_items)
+            dt = time.perf_counter() - t
+            if dt >= args.cpu_seconds / 4 or n >= tr.R:
+                break
+            n = int(min(tr.R, max(2 * n, n * (args.cpu_seconds / 2) / max(dt, 1e-3))))
+        line["cpu_baseline"] = {"value": round(n / dt, 1), "unit": "queries/s (scheduler)",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"the oracle's choice over the first {n} queries of "
+                                          f"the stream (hotness-aware policy), {dt:.1f} s"}
     print(json.dumps(line), flush=True)
 
 

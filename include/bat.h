@@ -345,10 +345,11 @@ bat_status bat_lse_merge(const float *o_parts, const float *lse_parts,
  * resident; user-prefix and item-prefix caches live in separate pools.  The
  * page gives no policy in detail.  These calls implement one plain reading,
  * query by query in arrival order:
- *   score  user mode: n_u (user resident), else n_u * requests_u when the
- *          user's blocks fit the user pool, else 0;
- *          item mode: T * sum over the query's m items of 1 (resident) or
- *          requests_i (missing, when the item pool has slots).
+ *   score  the prefix tokens that are hot: resident, or asked for by an
+ *          earlier query and able to stay resident.  User mode: n_u if the
+ *          user is resident, or was asked for before and its blocks fit the
+ *          user pool, else 0; item mode: T per item of the query that is
+ *          resident, or was asked for before while the item pool has slots.
  *          Item mode only on a strictly larger score (BAT_POLICY_HOTNESS);
  *          BAT_POLICY_USER_PREFIX always picks the user (the conventional
  *          baseline).  requests_x counts the earlier queries naming x.

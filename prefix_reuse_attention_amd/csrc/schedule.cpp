@@ -6,11 +6,12 @@
 // resident caches get reused, with user-prefix and item-prefix caches in
 // separate pools.  The page leaves the policy open; this file implements one
 // plain reading of it:
-//   * score, per query:  user mode = n_u if the user is resident, else
-//     n_u * (earlier requests of the user) when its blocks fit the user pool;
-//     item mode = T * sum over its items of (1 if resident, else earlier
-//     requests of the item, when the item pool has slots).  Item mode wins
-//     only on a larger score.  The user-as-prefix policy always picks user.
+//   * score, per query, the prefix tokens that are hot -- resident, or
+//     asked for by an earlier query and able to stay resident: user mode =
+//     n_u if the user is resident or was asked for before and its blocks fit
+//     the user pool; item mode = T per item that is resident or was asked
+//     for before while the item pool has slots.  Item mode wins only on a
+//     larger score.  The user-as-prefix policy always picks user.
 //   * the chosen prefix only is cached: user pool = least recently used
 //     eviction by blocks; item pool = lowest unused slot, else replace the
 //     resident item (not of this query) with the fewest earlier requests,
@@ -248,12 +249,12 @@ bat_status bat_sched_step(void *state, int32_t R, int32_t m, const int32_t *user
     // 2) choice
     bool item_mode = false;
     if (c.policy == BAT_POLICY_HOTNESS) {
-      const int64_t s_user = u_hit ? n_u : (fits ? n_u * s.ucount[u] : 0);
+      const int64_t s_user = (u_hit || (fits && s.ucount[u] > 0)) ? n_u : 0;
       int64_t s_item = 0;
       for (int32_t j = 0; j < m; ++j) {
         const int32_t i = its[j];
         if (s.slot[i] >= 0) s_item += T;
-        else if (c.item_capacity > 0) s_item += T * s.icount[i];
+        else if (c.item_capacity > 0 && s.icount[i] > 0) s_item += T;
       }
       item_mode = s_item > s_user;
     }

@@ -226,7 +226,7 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
                      int32_t max_prefix_len, void *out, float *lse, void *workspace,
                      size_t workspace_bytes, void *stream, bool prefix_only = false,
                      const float **part_o = nullptr, const float **part_lse = nullptr,
-                     int32_t H_kv = 0) {
+                     int32_t H_kv = 0, bool *self_key = nullptr) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -245,6 +245,12 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
 
   uint8_t *ws = (uint8_t *)workspace;
   p.prefix_only = prefix_only ? 1 : 0;
+  // prefix-only rows of single-token candidates: the ping-pong kernel folds
+  // each row's own key into its result and writes the final rows itself
+  if (self_key) {
+    *self_key = prefix_only && dt == BAT_BF16 && D == 128 && pl.waves == 8;
+    p.self_key = *self_key ? 1 : 0;
+  }
   if (part_o) *part_o = (const float *)(ws + pl.off_part_o);
   if (part_lse) *part_lse = (const float *)(ws + pl.off_part_lse);
   int32_t *hdr = (int32_t *)ws;
@@ -430,13 +436,16 @@ bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v
     return BAT_ERR_INVALID_ARG;
   const float *o_p = nullptr, *lse_p = nullptr;
   if (max_prefix_len > 0) {
-    // the prefix part of every row, as fp32 partials in the workspace
+    // the prefix part of every row, as fp32 partials in the workspace; for
+    // single-token candidates on the ping-pong kernel, the whole row at once
+    bool fused = false;
     const bat_status s = attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode,
                                    block_table, bt_stride, user_pool, item_pool, B, H, D, dt,
                                    softmax_scale, total_suffix, max_suffix_len, max_prefix_len,
                                    out, lse, workspace, workspace_bytes, stream, true, &o_p,
-                                   &lse_p);
+                                   &lse_p, 0, T == 1 ? &fused : nullptr);
     if (s != BAT_OK) return s;
+    if (fused) return BAT_OK;
   }
   // each candidate over its own tokens, merged with its row's prefix part
   const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);

@@ -59,6 +59,9 @@ struct AttnParams {
   int32_t chunk_len;              // prefix keys per chunk when split (0 = never)
   int32_t prefix_only;            // 1: rows see the prefix only; the kernels write fp32
                                   // partials at part_o / part_lse row q0 + row
+  int32_t self_key;               // with prefix_only: each row also sees its own suffix
+                                  // token (single-token candidates), and the kernel writes
+                                  // the final row to out / lse (ping-pong kernel only)
   int32_t max_prefix;             // host bound; longer prefixes are clamped to it
   const WorkItem *items;
   const ReqMeta *meta;
@@ -99,7 +102,7 @@ __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) 
   x.partial = x.n_chunks > 1;
   if (p.prefix_only) {  // never split: one partial row per suffix row
     x.with_suffix = false;
-    x.partial = true;
+    x.partial = !p.self_key;
     x.part_off = x.q0;
   }
   return x;

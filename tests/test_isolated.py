@@ -4,8 +4,11 @@ against the oracle, through the C ABI.
 Each suffix row sees its request's prefix and the T tokens of its own
 candidate.  Cases: every supported T, both bf16 head dims and fp32, user and
 item prefixes in one batch, empty prefixes and empty suffixes, the four- and
-eight-wave kernels (the ping-pong one for D=128), and the batch of
-single-token candidates of the 1024-history configuration on sampled rows.
+eight-wave kernels (the ping-pong one for D=128), the batch of single-token
+candidates of the 1024-history configuration on sampled rows, and
+single-token candidates on the ping-pong kernel, which folds each row's own
+key into its prefix result in one launch (ragged rows, a request with no
+prefix, user and item prefixes, and the 8k-history shape on sampled rows).
 Every expected value comes from the oracle.
 """
 import numpy as np
@@ -83,6 +86,38 @@ def test_isolated_single_token_candidates_1024_history(gpu_ready):
     req = np.searchsorted(wl.cu_s, rows, side="right") - 1
     k_p, v_p, cu_p = assemble_prefix(wl, np.unique(req))
     ref, ref_lse = oracle.prefill_isolated(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, T,
+                                           wl.scale, rows=rows, heads=heads)
+    check_close(got[rows, heads], ref, "bf16")
+    assert np.abs(lse[heads, rows] - ref_lse).max() <= 1e-3
+
+
+def test_isolated_single_token_fused_ping_pong(gpu_ready):
+    """T = 1 on the ping-pong kernel (bf16, D=128, 256-row items): the
+    row's own key is merged in the attention kernel's epilogue.  A request
+    with no prefix (its rows are their own token alone), an item prefix, a
+    ragged last row tile, a one-row request."""
+    wl = W.make_custom(dtype="bf16", H=2, D=128, n_s=[512, 264, 300, 8, 1],
+                       n_p=[700, 0, 129 * 4, 33, 64],
+                       mode=[W.USER, W.USER, W.ITEM, W.USER, W.USER], seed=170,
+                       num_items=300, name="iso_fused_T1")
+    assert wl.total_s >= 192 * wl.B  # the eight-wave (ping-pong) plan
+    _compare(wl, 1)
+
+
+@pytest.mark.slow
+def test_isolated_single_token_fused_8k_history_sampled(gpu_ready):
+    """The 8k-history configuration's shape (16 x 8192 prefix, 512 single-
+    token candidates each, H=16, D=128, bf16), on sampled (row, head) pairs."""
+    wl = W.make_config(4)
+    print("[isolated] config 4 shape, T=1, sampled", flush=True)
+    got, lse = _run_isolated(wl, 1)
+    rng = np.random.default_rng(171)
+    rows = np.concatenate([rng.integers(0, wl.total_s, 120), [0, wl.total_s - 1]])
+    rows = rows.astype(np.int32)
+    heads = rng.integers(0, wl.H, len(rows)).astype(np.int32)
+    req = np.searchsorted(wl.cu_s, rows, side="right") - 1
+    k_p, v_p, cu_p = assemble_prefix(wl, np.unique(req))
+    ref, ref_lse = oracle.prefill_isolated(wl.q, wl.k_s, wl.v_s, wl.cu_s, k_p, v_p, cu_p, 1,
                                            wl.scale, rows=rows, heads=heads)
     check_close(got[rows, heads], ref, "bf16")
     assert np.abs(lse[heads, rows] - ref_lse).max() <= 1e-3

@@ -290,9 +290,8 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel": (bf16_kernel_label(wl) if bf16 else f"attn_f32_kernel<{wl.D}>")
-                               + (" + item_local_kernel (merge)"
-                                  if isolated and "pp_kernel" not in bf16_kernel_label(wl)
-                                  else (" (own key folded in)" if isolated else "")),
+                               + ((" (own key folded in)" if bf16
+                                   else " + item_local_kernel (merge)") if isolated else ""),
                      "kernel_ms_mean": round(kernel_ms, 5)},
         "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
                      "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),

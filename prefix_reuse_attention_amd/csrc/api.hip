@@ -245,10 +245,10 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
 
   uint8_t *ws = (uint8_t *)workspace;
   p.prefix_only = prefix_only ? 1 : 0;
-  // prefix-only rows of single-token candidates: the ping-pong kernel folds
-  // each row's own key into its result and writes the final rows itself
+  // prefix-only rows of single-token candidates: the bf16 kernels fold each
+  // row's own key into its result and write the final rows themselves
   if (self_key) {
-    *self_key = prefix_only && dt == BAT_BF16 && D == 128 && pl.waves == 8;
+    *self_key = prefix_only && dt == BAT_BF16;
     p.self_key = *self_key ? 1 : 0;
   }
   if (part_o) *part_o = (const float *)(ws + pl.off_part_o);
@@ -437,7 +437,7 @@ bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v
   const float *o_p = nullptr, *lse_p = nullptr;
   if (max_prefix_len > 0) {
     // the prefix part of every row, as fp32 partials in the workspace; for
-    // single-token candidates on the ping-pong kernel, the whole row at once
+    // single-token bf16 candidates, the whole row at once
     bool fused = false;
     const bat_status s = attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode,
                                    block_table, bt_stride, user_pool, item_pool, B, H, D, dt,

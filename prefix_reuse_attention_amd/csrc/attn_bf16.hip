@@ -103,6 +103,75 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Candidate-isolated rows of single-token candidates: the row sees its
+// request's prefix and its own token.  The prefix part arrives as the
+// kernel's running state (unnormalised o with row sum l_tot over 2^(s - m)
+// in the log2 domain); the own key is one more score, merged exactly:
+//     s = scale * <q, k_self>,  lse = log2(2^(m + log2 l_tot) + 2^s),
+//     out = (o + 2^(s - m) v_self) / (l_tot + 2^(s - m))  (in safe form).
+// The lane pair (lane, lane ^ 32) of a row holds the output elements
+// 32*nd + 8*j + 4*hf + e; each lane reads the same elements of q, k_self and
+// v_self (8-byte pieces), the pair sums the dot product with one shuffle.
+// l_tot == 0 (no prefix keys) leaves the own token alone.
+template <int D>
+__device__ __forceinline__ void write_with_self_key(const AttnParams &p, int64_t qrow, int head,
+                                                    int kv_head, int hf,
+                                                    const f32x16 (&o)[D / 32], float m_run,
+                                                    float l_tot) {
+  constexpr int ND = D / 32;
+  const uint16_t *qp = (const uint16_t *)p.q + (qrow * p.H + head) * D + 4 * hf;
+  const uint16_t *kp = (const uint16_t *)p.k + (qrow * p.H_kv + kv_head) * D + 4 * hf;
+  const uint16_t *vp = (const uint16_t *)p.v + (qrow * p.H_kv + kv_head) * D + 4 * hf;
+  u32x2 vw[ND][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = 32 * nd + 8 * j;
+      const u32x2 qw = *(const u32x2 *)(qp + off);
+      const u32x2 kw = *(const u32x2 *)(kp + off);
+      vw[nd][j] = *(const u32x2 *)(vp + off);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t a = qw[w], b = kw[w];
+        dot = __builtin_fmaf(__builtin_bit_cast(float, a << 16),
+                             __builtin_bit_cast(float, b << 16), dot);
+        dot = __builtin_fmaf(__builtin_bit_cast(float, a & 0xffff0000u),
+                             __builtin_bit_cast(float, b & 0xffff0000u), dot);
+      }
+    }
+  dot += __shfl_xor(dot, 32);
+  const float s2 = dot * p.scale_log2;
+  const bool have = l_tot > 0.f;
+  const float lp = have ? m_run + __log2f(l_tot) : s2;
+  const float mx = fmaxf(lp, s2);
+  const float wp = have ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
+  const float wc = __builtin_amdgcn_exp2f(s2 - mx);
+  const float iw = 1.0f / (wp + wc);
+  const float a = have ? wp * iw / l_tot : 0.f, b = wc * iw;
+  uint16_t *out = (uint16_t *)p.out + (qrow * p.H + head) * D + 4 * hf;
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v[4];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t x = vw[nd][j][w];
+        v[2 * w] = __builtin_bit_cast(float, x << 16);
+        v[2 * w + 1] = __builtin_bit_cast(float, x & 0xffff0000u);
+      }
+      u32x2 w;
+      w[0] = pack_bf16x2(a * o[nd][4 * j + 0] + b * v[0], a * o[nd][4 * j + 1] + b * v[1]);
+      w[1] = pack_bf16x2(a * o[nd][4 * j + 2] + b * v[2], a * o[nd][4 * j + 3] + b * v[3]);
+      *(u32x2 *)(out + 32 * nd + 8 * j) = w;
+    }
+  if (p.lse && hf == 0)
+    p.lse[(int64_t)head * p.total_s + qrow] = (mx + __log2f(wp + wc)) * 0.69314718055994530942f;
+}
+
+
 __device__ __forceinline__ float row_max_both_halves(float v) {
   // v_permlane32_swap(v, v) leaves {own, other half} in its two results
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
@@ -588,8 +657,19 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.init_lanes();
   const int n_tiles = cp.n_tiles_p + (x.with_suffix ? (x.n_s + C::BN - 1) / C::BN : 0);
   // prefix-only rows of a request with no prefix: no keys, nothing to write
-  // (the merge that follows reads that partial as empty)
-  if (n_tiles == 0) return;
+  // (the merge that follows reads that partial as empty); with the row's own
+  // key folded in, the row is that key alone
+  if (n_tiles == 0) {
+    if (p.self_key && row_ok) {
+      f32x16 z[C::ND];
+#pragma unroll
+      for (int nd = 0; nd < C::ND; ++nd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[nd][i] = 0.f;
+      write_with_self_key<D>(p, x.q0 + row, head, cp.head, hf, z, 0.f, 0.f);
+    }
+    return;
+  }
   cp.n_tiles = n_tiles;
   __shared__ u32x4 s_tab[TileCopy<D, W, FLAT>::kTabTiles];
   cp.tab = s_tab;
@@ -659,6 +739,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   const float inv = 1.0f / l_tot;
   const float lse_nat = (sm.m_run + log2f(l_tot)) * 0.69314718055994530942f;
   if (!row_ok) return;
+  if (p.self_key) {
+    write_with_self_key<D>(p, x.q0 + row, head, cp.head, hf, o, sm.m_run, l_tot);
+    return;
+  }
   if (!x.partial) {
     uint16_t *out = (uint16_t *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D;
 #pragma unroll
@@ -684,74 +768,6 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
       }
     if (hf == 0) p.part_lse[pr * p.H + head] = lse_nat;
   }
-}
-
-// Candidate-isolated rows of single-token candidates: the row sees its
-// request's prefix and its own token.  The prefix part arrives as the
-// kernel's running state (unnormalised o with row sum l_tot over 2^(s - m)
-// in the log2 domain); the own key is one more score, merged exactly:
-//     s = scale * <q, k_self>,  lse = log2(2^(m + log2 l_tot) + 2^s),
-//     out = (o + 2^(s - m) v_self) / (l_tot + 2^(s - m))  (in safe form).
-// The lane pair (lane, lane ^ 32) of a row holds the output elements
-// 32*nd + 8*j + 4*hf + e; each lane reads the same elements of q, k_self and
-// v_self (8-byte pieces), the pair sums the dot product with one shuffle.
-// l_tot == 0 (no prefix keys) leaves the own token alone.
-template <int D>
-__device__ __forceinline__ void write_with_self_key(const AttnParams &p, int64_t qrow, int head,
-                                                    int kv_head, int hf,
-                                                    const f32x16 (&o)[D / 32], float m_run,
-                                                    float l_tot) {
-  constexpr int ND = D / 32;
-  const uint16_t *qp = (const uint16_t *)p.q + (qrow * p.H + head) * D + 4 * hf;
-  const uint16_t *kp = (const uint16_t *)p.k + (qrow * p.H_kv + kv_head) * D + 4 * hf;
-  const uint16_t *vp = (const uint16_t *)p.v + (qrow * p.H_kv + kv_head) * D + 4 * hf;
-  u32x2 vw[ND][4];
-  float dot = 0.f;
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = 32 * nd + 8 * j;
-      const u32x2 qw = *(const u32x2 *)(qp + off);
-      const u32x2 kw = *(const u32x2 *)(kp + off);
-      vw[nd][j] = *(const u32x2 *)(vp + off);
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t a = qw[w], b = kw[w];
-        dot = __builtin_fmaf(__builtin_bit_cast(float, a << 16),
-                             __builtin_bit_cast(float, b << 16), dot);
-        dot = __builtin_fmaf(__builtin_bit_cast(float, a & 0xffff0000u),
-                             __builtin_bit_cast(float, b & 0xffff0000u), dot);
-      }
-    }
-  dot += __shfl_xor(dot, 32);
-  const float s2 = dot * p.scale_log2;
-  const bool have = l_tot > 0.f;
-  const float lp = have ? m_run + __log2f(l_tot) : s2;
-  const float mx = fmaxf(lp, s2);
-  const float wp = have ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
-  const float wc = __builtin_amdgcn_exp2f(s2 - mx);
-  const float iw = 1.0f / (wp + wc);
-  const float a = have ? wp * iw / l_tot : 0.f, b = wc * iw;
-  uint16_t *out = (uint16_t *)p.out + (qrow * p.H + head) * D + 4 * hf;
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v[4];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t x = vw[nd][j][w];
-        v[2 * w] = __builtin_bit_cast(float, x << 16);
-        v[2 * w + 1] = __builtin_bit_cast(float, x & 0xffff0000u);
-      }
-      u32x2 w;
-      w[0] = pack_bf16x2(a * o[nd][4 * j + 0] + b * v[0], a * o[nd][4 * j + 1] + b * v[1]);
-      w[1] = pack_bf16x2(a * o[nd][4 * j + 2] + b * v[2], a * o[nd][4 * j + 3] + b * v[3]);
-      *(u32x2 *)(out + 32 * nd + 8 * j) = w;
-    }
-  if (p.lse && hf == 0)
-    p.lse[(int64_t)head * p.total_s + qrow] = (mx + __log2f(wp + wc)) * 0.69314718055994530942f;
 }
 
 template <typename F, int... J>

@@ -61,7 +61,7 @@ struct AttnParams {
                                   // partials at part_o / part_lse row q0 + row
   int32_t self_key;               // with prefix_only: each row also sees its own suffix
                                   // token (single-token candidates), and the kernel writes
-                                  // the final row to out / lse (ping-pong kernel only)
+                                  // the final row to out / lse (bf16 kernels only)
   int32_t max_prefix;             // host bound; longer prefixes are clamped to it
   const WorkItem *items;
   const ReqMeta *meta;

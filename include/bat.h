@@ -293,7 +293,9 @@ size_t bat_attn_isolated_workspace_size(int32_t B, int32_t H, int32_t D,
  * + c*T + T-1; every request's suffix length must be a multiple of T (the
  * result is unspecified otherwise).  Computed as the prefix part of every
  * row (the attention kernels over the prefix only, fp32 partials in the
- * workspace) merged exactly with each candidate's own part.
+ * workspace) merged exactly with each candidate's own part; for T = 1 in
+ * bf16 the attention kernel folds the row's own key into its prefix result
+ * and writes the row in the same launch.
  *
  *   Arguments as bat_attn_prefill, plus
  *   tokens_per_candidate  T, one of 1, 2, 4, 8 (else BAT_ERR_UNSUPPORTED);

@@ -47,19 +47,25 @@ struct Header {
   int32_t lru_head, lru_tail;
   int32_t next_free;      // lowest slot never used
   int32_t heap_size;
-  // offsets (bytes from the start of the state) of the arrays below
-  int64_t off_user_len, off_user_prev, off_user_next, off_user_count, off_user_res;
-  int64_t off_item_slot, off_item_pos, off_item_count, off_item_last, off_item_stamp,
-      off_item_pin, off_slot_item, off_heap;
+  // offsets (bytes from the start of the state) of the arrays, in Array order
+  int64_t off[13];
   uint64_t magic;
 };
+
+// The state's arrays: per user, per item, per item slot.
+enum Array {
+  kUserLen, kUserPrev, kUserNext, kUserCount, kUserRes,
+  kItemSlot, kItemPos, kItemCount, kItemLast, kItemStamp, kItemPin,
+  kSlotItem, kHeap, kNumArrays
+};
+static_assert(kNumArrays == 13, "one offset per array");
 
 constexpr uint64_t kMagic = 0x6261747363686431ull;  // "batschd1"
 
 inline int64_t align_up(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 struct Layout {
-  int64_t off[13];
+  int64_t off[kNumArrays];
   int64_t total;
 };
 
@@ -69,11 +75,11 @@ bool make_layout(const bat_sched_config *c, Layout &L) {
       (c->policy != BAT_POLICY_USER_PREFIX && c->policy != BAT_POLICY_HOTNESS))
     return false;
   const int64_t U = c->num_users, N = c->num_items, C = c->item_capacity;
-  const int64_t sizes[13] = {U * 4, U * 4, U * 4, U * 8, U * 1,           // users
-                             N * 4, N * 4, N * 8, N * 8, N * 8, N * 1,    // items
-                             C * 4, C * 4};                               // slots, heap
+  const int64_t sizes[kNumArrays] = {U * 4, U * 4, U * 4, U * 8, U * 1,           // users
+                                     N * 4, N * 4, N * 8, N * 8, N * 8, N * 1,    // items
+                                     C * 4, C * 4};                               // slots
   int64_t at = align_up(sizeof(Header));
-  for (int i = 0; i < 13; ++i) {
+  for (int i = 0; i < kNumArrays; ++i) {
     L.off[i] = at;
     at = align_up(at + sizes[i]);
   }
@@ -94,19 +100,19 @@ struct State {
   explicit State(void *base) {
     uint8_t *b = static_cast<uint8_t *>(base);
     h = reinterpret_cast<Header *>(b);
-    user_len = reinterpret_cast<int32_t *>(b + h->off_user_len);
-    prev = reinterpret_cast<int32_t *>(b + h->off_user_prev);
-    next = reinterpret_cast<int32_t *>(b + h->off_user_next);
-    ucount = reinterpret_cast<int64_t *>(b + h->off_user_count);
-    ures = b + h->off_user_res;
-    slot = reinterpret_cast<int32_t *>(b + h->off_item_slot);
-    pos = reinterpret_cast<int32_t *>(b + h->off_item_pos);
-    icount = reinterpret_cast<int64_t *>(b + h->off_item_count);
-    last = reinterpret_cast<int64_t *>(b + h->off_item_last);
-    stamp = reinterpret_cast<int64_t *>(b + h->off_item_stamp);
-    pin = b + h->off_item_pin;
-    slot_item = reinterpret_cast<int32_t *>(b + h->off_slot_item);
-    heap = reinterpret_cast<int32_t *>(b + h->off_heap);
+    user_len = reinterpret_cast<int32_t *>(b + h->off[kUserLen]);
+    prev = reinterpret_cast<int32_t *>(b + h->off[kUserPrev]);
+    next = reinterpret_cast<int32_t *>(b + h->off[kUserNext]);
+    ucount = reinterpret_cast<int64_t *>(b + h->off[kUserCount]);
+    ures = b + h->off[kUserRes];
+    slot = reinterpret_cast<int32_t *>(b + h->off[kItemSlot]);
+    pos = reinterpret_cast<int32_t *>(b + h->off[kItemPos]);
+    icount = reinterpret_cast<int64_t *>(b + h->off[kItemCount]);
+    last = reinterpret_cast<int64_t *>(b + h->off[kItemLast]);
+    stamp = reinterpret_cast<int64_t *>(b + h->off[kItemStamp]);
+    pin = b + h->off[kItemPin];
+    slot_item = reinterpret_cast<int32_t *>(b + h->off[kSlotItem]);
+    heap = reinterpret_cast<int32_t *>(b + h->off[kHeap]);
   }
 
   // ---- user pool: LRU list, head = most recent ----
@@ -196,8 +202,7 @@ bat_status bat_sched_init(const bat_sched_config *cfg, const int32_t *user_len, 
   Header *h = static_cast<Header *>(state);
   h->cfg = *cfg;
   h->lru_head = h->lru_tail = -1;
-  int64_t *o = &h->off_user_len;
-  for (int i = 0; i < 13; ++i) o[i] = L.off[i];
+  for (int i = 0; i < kNumArrays; ++i) h->off[i] = L.off[i];
   h->magic = kMagic;
   State s(state);
   for (int32_t u = 0; u < cfg->num_users; ++u) {

@@ -296,3 +296,24 @@ def test_native_matches_oracle_under_eviction_pressure():
     assert (kept > 0).any() and (kept < missing).any(), "no admissions or no rejections"
     ever = set(tr.user[(got["mode"] == S.MODE_USER) & (got["user_hit"] == 0)].tolist())
     assert len(got["resident_users"]) < len(ever), "no user evictions"
+
+
+def test_native_scheduler_under_host_sanitizers(tmp_path):
+    """The scheduler's C++ built for the host with AddressSanitizer and
+    UBSan, driven over random configurations and traces
+    (tests/sched_sanitize_driver.cpp): no out-of-bounds access, no undefined
+    behaviour, bad queries rejected."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "drv")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "sched_sanitize_driver.cpp"),
+                    os.path.join(root, "prefix_reuse_attention_amd", "csrc", "schedule.cpp"),
+                    "-o", exe], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "asan driver ok" in r.stdout

@@ -10,7 +10,9 @@
  * (section "Why it works", the disaggregated cache pool).  This library is
  * the data-parallel hot path of that method on one GPU: building the paged
  * prefix cache, and prefill attention of the fresh (suffix) tokens over the
- * cached prefix plus their own group.
+ * cached prefix plus their own group.  Around it: prefix rows (how the next
+ * layer's cache is built), candidate-isolated suffixes, grouped key/value
+ * heads, and a host-side choice of each query's prefix mode (bat_sched_*).
  *
  * Attention semantics (identical in both prefix modes): scaled dot-product
  * softmax, no positional encoding, no causal mask.  For request r and head h

@@ -317,3 +317,21 @@ def test_native_scheduler_under_host_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "asan driver ok" in r.stdout
+
+
+def test_native_matches_oracle_on_measured_traffic_prefix():
+    """The measured traffic's shape and budget (20000 users Zipf(0.9) with
+    U[256, 4096]-token histories, 128 of 20000 items Zipf(1.1), 2^21 cache
+    tokens of which 8192 item slots), on the first 1000 queries of the same
+    seeded stream: the oracle's pace bounds the sample."""
+    n = 1000
+    tr = W.make_traffic(7, n, 20000, num_items=20000, items_per_request=128,
+                        user_len_range=(256, 4096), user_zipf_s=0.9, item_zipf_s=1.1)
+    T, bs, budget, slots = 4, 64, 1 << 21, 8192
+    for policy, ucap, icap in ((S.POLICY_HOTNESS, (budget - slots * T) // bs, slots),
+                               (S.POLICY_USER_PREFIX, budget // bs, 0)):
+        ref = S.schedule(tr.user, tr.user_len, tr.items, T, bs, ucap, icap, policy,
+                         num_items=tr.num_items)
+        got = _native(tr.user, tr.user_len, tr.items, T, bs, ucap, icap, policy,
+                      tr.num_items, chunks=(0.5,))
+        _same(got, ref)

@@ -579,10 +579,7 @@ def bench_schedule_workload(args):
     attention work each policy's choices imply run through the library's
     kernels, timed per window.  One JSON line; `value` is queries per second
     of the hotness-aware window's attention work."""
-    import numpy as np
     import torch
-    from prefix_reuse_attention_amd import api
-    from prefix_reuse_attention_amd import workloads as W
     c = SCHED
     t = time.perf_counter()
     tr = _traffic(c)

@@ -208,7 +208,7 @@ def _native(tr_user, user_len, items, T, block, ucap, icap, policy, num_items, c
     from prefix_reuse_attention_amd import api
     sch = api.Scheduler(policy, T, block, ucap, icap, user_len, num_items)
     R = len(tr_user)
-    parts, at = [], 0
+    parts = []
     cuts = sorted({0, R, *[int(R * c) for c in chunks]})
     for a, b in zip(cuts, cuts[1:]):
         parts.append(sch.step(tr_user[a:b], items[a:b]))

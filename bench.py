@@ -63,10 +63,11 @@ def _pmc_kib(run_dir, counter, name_part):
 
 def bf16_kernel_label(wl):
     """The bf16 kernel the library launches for this workload: eight waves
-    (256 rows per item) when suffixes average at least 192 rows, else four;
+    (256 rows per item) when suffixes average at least 192 rows (and, at
+    D=64, the longest prefix has at least 4096 keys), else four;
     with eight waves and head dim 128 the ping-pong kernel.  Buffer-load
     gathers (pools under 2 GiB)."""
-    waves = 8 if wl.total_s >= 192 * wl.B else 4
+    waves = 8 if wl.total_s >= 192 * wl.B and (wl.D == 128 or int(wl.n_p.max()) >= 4096) else 4
     if waves == 8 and wl.D == 128:
         return "attn_bf16_pp_kernel<128, false>"
     return f"attn_bf16_kernel<{wl.D}, {waves}, false>"

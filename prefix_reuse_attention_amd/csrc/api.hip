@@ -80,11 +80,14 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
-  // long enough to fill them, else four (128 rows)
+  // long enough to fill them, else four (128 rows).  At D=64 the shared tile
+  // only pays with long prefixes (measured: eight waves ahead from about
+  // 4096 prefix keys, four ahead below)
   if (const char *e = std::getenv("BAT_WAVES")) {
     pl.waves = std::atoi(e) == 8 ? 8 : 4;
   } else {
-    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B) ? 8 : 4;
+    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B && (D == 128 || max_p >= 4096))
+                   ? 8 : 4;
   }
   // BAT_GATHER=flat: the per-key gather of small pool blocks always takes
   // the global-load form that pools of 2 GiB or more need

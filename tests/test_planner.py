@@ -46,7 +46,10 @@ def _check(wl, hdr, raw, H=None, hg=1):
     """H query heads (wl.H by default), hg of them per key/value head."""
     B, H = wl.B, (wl.H if H is None else H)
     total_s = int(wl.n_s.sum())
-    bm = 256 if total_s >= 192 * B else 128
+    # eight-wave (256-row) items when suffixes average 192 rows or more and,
+    # at head dim 64, the longest prefix has at least 4096 keys
+    eight = total_s >= 192 * B and (wl.D == 128 or int(wl.n_p.max()) >= 4096)
+    bm = 256 if eight else 128
     max_s = int(wl.n_s.max())
     t_max = -(-max_s // bm)
     grid = 8 * (-(-((H // hg) * B) // 8)) * hg * t_max
@@ -92,13 +95,16 @@ def _check(wl, hdr, raw, H=None, hg=1):
         assert all(a >= b for a, b in zip(seq, seq[1:])), f"XCD {x} not longest first"
 
 
-@pytest.mark.parametrize("B,seed", [(3, 1), (16, 2), (100, 3), (256, 4), (300, 5)])
-def test_plan_items(gpu_ready, monkeypatch, B, seed):
+@pytest.mark.parametrize("B,seed,D", [(3, 1, 64), (16, 2, 64), (100, 3, 64), (256, 4, 64),
+                                      (300, 5, 64), (100, 8, 128), (300, 9, 128)])
+def test_plan_items(gpu_ready, monkeypatch, B, seed, D):
+    """Head dim 64 plans 128-row items here (short prefixes), head dim 128
+    256-row items: both item sizes on both planner paths."""
     rng = np.random.default_rng(1000 + seed)
     n_s = rng.integers(1, 600, size=B)
     n_s[rng.random(B) < 0.1] = 0        # some empty suffixes
     n_p = rng.integers(0, 700, size=B)
-    wl = W.make_custom(dtype="bf16", H=2, D=64, n_s=n_s.tolist(), n_p=n_p.tolist(),
+    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s.tolist(), n_p=n_p.tolist(),
                        mode=[W.USER] * B, seed=seed, user_block_size=64,
                        name=f"plan_B{B}")
     print(f"[planner] B={B} total_s={int(n_s.sum())}", flush=True)

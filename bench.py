@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--workload", choices=("prefill", "isolated", "gqa", "prefix-rows",
-                                           "item-local", "schedule"),
+                                           "item-local", "schedule", "split"),
                     default="prefill",
                     help="prefill: bat_attn_prefill on --config (the default line); "
                          "isolated: bat_attn_prefill_isolated on --config with single-token "
@@ -110,7 +110,9 @@ def main():
                          "key/value heads for its 16 query heads; prefix-rows: bat_attn_prefix_rows over the 8k-history "
                          "prefixes; item-local: bat_attn_item_local over the 20000-item pool; "
                          "schedule: the prefix-mode choice (bat_sched_*) on Zipf traffic and "
-                         "the attention work it implies for a window of queries")
+                         "the attention work it implies for a window of queries; split: "
+                         "bat_attn_prefill on 2 requests with 32768-token prefixes, which "
+                         "the planner splits into chunks merged by log-sum-exp")
     ap.add_argument("--host-sweep", action="store_true",
                     help="with --workload schedule: only the host accounting of both policies "
                          "over a grid of traffic shapes (no GPU needed)")
@@ -171,6 +173,12 @@ def main():
                            mode=[W.USER] * 16, seed=104, user_block_size=64, name="config4_gqa")
         wl.notes["description"] = ("bf16, B=16, 16 query heads over 4 key/value heads, D=128, "
                                    "user prefix 8192 (64-token pages), suffix 512")
+    elif args.workload == "split":
+        # too few items to fill the GPU unsplit: prefix chunks + merge launch
+        wl = W.make_custom(dtype="bf16", H=16, D=128, n_s=[512] * 2, n_p=[32768] * 2,
+                           mode=[W.USER] * 2, seed=105, user_block_size=64, name="split_32k")
+        wl.notes["description"] = ("bf16, B=2, H=16, D=128, user prefix 32768 (64-token pages), "
+                                   "suffix 512; prefixes split into chunks")
     else:
         wl = W.make_config(args.config)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",
@@ -259,7 +267,7 @@ def main():
           f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     base = None
-    if not args.no_cpu_baseline and not isolated and not gqa_heads:
+    if not args.no_cpu_baseline and not isolated and not gqa_heads and args.workload != "split":
         base = run_cpu_baseline(wl, args.cpu_seconds)
 
     line = {

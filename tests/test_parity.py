@@ -173,3 +173,19 @@ def test_config_full_size_sampled(gpu_ready, k):
     # properties that hold for every row: finite, and a convex combination of
     # values whose entries are bounded by the largest |v|
     assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.slow
+def test_split_32k_prefix_sampled(gpu_ready):
+    """The split-prefix workload the bench times (2 requests x 32768-token
+    prefix, suffix 512, H=16, D=128, bf16): 8 chunks per prefix merged by
+    log-sum-exp, on sampled (row, head) pairs."""
+    wl = W.make_custom(dtype="bf16", H=16, D=128, n_s=[512] * 2, n_p=[32768] * 2,
+                       mode=[W.USER] * 2, seed=105, user_block_size=64, name="split_32k")
+    print("[parity] split 32k prefixes, sampled", flush=True)
+    got, lse = _run(wl)
+    rows, heads = sample_pairs(wl, 200, seed=106)
+    ref_o, ref_l = oracle_sampled(wl, rows, heads)
+    check_close(got[rows, heads], ref_o, "bf16", strict_abs=4e-3, what="split_32k out")
+    assert np.abs(lse[heads, rows] - ref_l).max() <= 1e-3
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))

@@ -73,6 +73,90 @@ def test_hand_kv_scatter():
     np.testing.assert_array_equal(pool[:, 0, :, 0], np.array(g["pool"]))
 
 
+def test_hand_item_prefix():
+    """The item-mode prefix of two requests worked by hand, both from the
+    item-major token array and from a pool whose items sit at permuted
+    physical slots (read slot by slot through the slot-valued table row)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_item_prefix.json")))
+    T = g["tokens_per_item"]
+    x = np.array(g["item_tokens"], dtype=np.int32).reshape(-1, 1, 1)
+    for ids, want in zip(g["requests"], g["prefixes"]):
+        got = oracle.gather_item_prefix(x, ids, T)
+        assert got.shape == (len(want), 1, 1)
+        np.testing.assert_array_equal(got[:, 0, 0], want)
+    n_items = len(g["slot_of_item"])
+    cu = np.arange(0, (n_items + 1) * T, T)
+    pool = oracle.kv_scatter(x, cu, np.array(g["slot_of_item"]).reshape(-1, 1), n_items, T, -1)
+    np.testing.assert_array_equal(pool[:, 0, :, 0], np.array(g["pool_slots"]))
+    for slots, want in zip(g["requests_as_slots"], g["prefixes"]):
+        np.testing.assert_array_equal(np.concatenate([pool[s, 0, :, 0] for s in slots]), want)
+
+
+def test_item_prefix_equals_reading_the_scattered_pool():
+    """gather_item_prefix over item-major tokens equals reading, head by head,
+    the pool kv_scatter builds with the items at permuted physical slots,
+    through those items' slots (distinct ids, a repeated id, every id)."""
+    rng = np.random.default_rng(41)
+    n_items, T, H, D = 9, 4, 3, 5
+    tok = rng.standard_normal((n_items * T, H, D))
+    slot = rng.permutation(n_items)
+    cu = np.arange(0, (n_items + 1) * T, T)
+    pool = oracle.kv_scatter(tok, cu, slot.reshape(-1, 1), n_items, T, np.nan)
+    for ids in (rng.choice(n_items, 5, replace=False), np.array([3, 3, 0]), np.arange(n_items)):
+        want = oracle.gather_item_prefix(tok, ids, T)
+        assert want.shape == (len(ids) * T, H, D)
+        for h in range(H):
+            got = np.concatenate([pool[slot[i], h] for i in ids])
+            np.testing.assert_array_equal(got, want[:, h])
+
+
+def test_bf16_widening_worked_values():
+    """bfloat16 bit patterns worked by hand (sign, 8-bit exponent biased by
+    127, 7 stored mantissa bits) widen to these exact values in both oracle
+    paths: the numpy widening of the isolated rows and the C loader (through
+    a one-key attention, whose output is that key's value)."""
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x4049, 0x0000, 0xBF40, 0x4300], np.uint16)
+    want = np.array([1.0, -2.0, 0.25, 3.140625, 0.0, -0.75, 128.0])
+    np.testing.assert_array_equal(oracle._widen(bits), want)
+    v = bits.reshape(1, -1)
+    out, _ = oracle.attention_masked(np.zeros_like(v), np.zeros_like(v), v,
+                                     np.ones((1, 1), bool), 1.0)
+    np.testing.assert_array_equal(out[0], want)
+
+
+def test_isolated_bf16_inputs_brute_force():
+    """prefill_isolated on bfloat16 bit patterns against explicit loops over
+    the values those patterns hold.  The values are multiples of 1/8 in
+    [-2, 2], exact in bfloat16, so their bits are the float32 bits' upper
+    half and the loops take the values themselves (no bf16 conversion code
+    on the reference side)."""
+    rng = np.random.default_rng(36)
+    T, H, D, scale = 2, 2, 4, 0.4
+    lens_p, lens_s = [3, 0, 4], [4, 2, 2]
+    vals = {n: rng.integers(-16, 17, size=(sum(lens_p if n in ("kp", "vp") else lens_s), H, D)) / 8.0
+            for n in ("q", "ks", "vs", "kp", "vp")}
+    bits = {n: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            for n, a in vals.items()}
+    cu_p = np.concatenate([[0], np.cumsum(lens_p)]).astype(np.int32)
+    cu_s = np.concatenate([[0], np.cumsum(lens_s)]).astype(np.int32)
+    out, lse = oracle.prefill_isolated(bits["q"], bits["ks"], bits["vs"], cu_s, bits["kp"],
+                                       bits["vp"], cu_p, T, scale)
+    for r in range(len(lens_s)):
+        for i in range(cu_s[r], cu_s[r + 1]):
+            c0 = cu_s[r] + ((i - cu_s[r]) // T) * T
+            for h in range(H):
+                keys = [vals["kp"][j, h] for j in range(cu_p[r], cu_p[r + 1])] + \
+                       [vals["ks"][j, h] for j in range(c0, c0 + T)]
+                vv = [vals["vp"][j, h] for j in range(cu_p[r], cu_p[r + 1])] + \
+                     [vals["vs"][j, h] for j in range(c0, c0 + T)]
+                sc = [scale * sum(float(vals["q"][i, h, d]) * float(kk[d]) for d in range(D))
+                      for kk in keys]
+                z = sum(math.exp(x) for x in sc)
+                ref = sum(math.exp(x) / z * w for x, w in zip(sc, vv))
+                np.testing.assert_allclose(out[i, h], ref, rtol=0, atol=1e-12)
+                assert abs(lse[h, i] - math.log(z)) <= 1e-12
+
+
 # ---------------------------------------------------------------- brute force
 @pytest.mark.parametrize("n_p", [0, 1, 3, 17])
 @pytest.mark.parametrize("n_s", [1, 2, 5])

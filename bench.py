@@ -265,6 +265,8 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events: mean "
           f"{kernel_ms:.4f}, min {per_call_ms.min():.4f}, p90 {np.percentile(per_call_ms, 90):.4f})"
           f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    print("[bench] per-call ms: " + " ".join(f"{v:.4f}" for v in per_call_ms),
+          file=sys.stderr, flush=True)
 
     base = None
     if not args.no_cpu_baseline and not isolated and not gqa_heads and args.workload != "split":

@@ -3,10 +3,11 @@
  * library, libbat.so.
  *
  * The method is the one the Bat page ("Bat: Efficient Generative Recommender
- * Serving with Bipartite Attention") describes: user and item tokens are
- * order-agnostic, so either group may be the prompt prefix whose key/value
- * cache is built once and reused (sections "This paper's idea", "Why it
- * works"), and user-prefix and item-prefix caches live in separate pools
+ * Serving with Bipartite Attention") describes (sections "This paper's idea",
+ * "Why it works"): a recommendation prompt holds a user's history and a set
+ * of items, neither carrying positions, so the two groups can trade places,
+ * and whichever one comes first has its key/value cache computed once and
+ * served again; user-prefix and item-prefix caches are kept in separate pools
  * (section "Why it works", the disaggregated cache pool).  This library is
  * the data-parallel hot path of that method on one GPU: building the paged
  * prefix cache, and prefill attention of the fresh (suffix) tokens over the
@@ -37,13 +38,38 @@
  *   - Errors: a bat_status is returned; nothing is thrown across the ABI.
  *     Host-detectable argument errors return before anything is enqueued.
  *     With the environment variable BAT_VALIDATE=1 the library also checks
- *     block ids and lengths on the device, synchronises the stream and
- *     returns BAT_ERR_BLOCK_TABLE on a violation.  Without it, an
- *     out-of-range block id is never dereferenced (the kernels treat its
- *     tokens as zero keys/values, or skip the write) but the result is
+ *     on the device, synchronises the stream and returns
+ *     BAT_ERR_BLOCK_TABLE when any of these fails:
+ *       - every block id read lies in [0, num_blocks) of its pool;
+ *       - a suffix length is in [0, max_suffix_len] and cu_suffix_lens[r+1]
+ *         <= total_suffix (bat_attn_prefix_rows: the prefix lengths against
+ *         max_prefix_len);
+ *       - a prefix length is in [0, max_prefix_len] and fits its block-table
+ *         row: prefix_lens[r] <= bt_stride * block_size of its pool;
+ *       - bat_kv_build: cu_lens is non-decreasing up to total_tokens and each
+ *         request's tokens fit its block-table row.
+ *     Without it, the same violations are never dereferenced (a prefix
+ *     longer than max_prefix_len is cut to it, an out-of-range block id
+ *     reads as zero keys/values or is not written) but the result is
  *     unspecified.
  *   - Thread safety: calls are independent; concurrent calls must not share
- *     a workspace.
+ *     a workspace.  Validated calls on different streams or threads report
+ *     only their own violations.
+ *   - Environment variables, read on every call (tests use them to reach
+ *     every kernel form; none changes what is computed, only how):
+ *       BAT_VALIDATE=1       the device checks above
+ *       BAT_WAVES=4|8        bf16 rows per work item: 4 or 8 waves of 32 rows
+ *                            (default: 8 when suffixes average >= 192 rows
+ *                            and, at D=64, the longest prefix has >= 4096
+ *                            keys; else 4)
+ *       BAT_GATHER=flat      per-key gathers of small pool blocks by global
+ *                            loads (the form pools of 2 GiB or more take)
+ *                            instead of buffer loads
+ *       BAT_SPLIT_CHUNK=n    split every prefix into chunks of n keys
+ *                            (rounded up to the key tile) merged by
+ *                            log-sum-exp; a value above every prefix never
+ *                            splits (default: split only when the batch has
+ *                            too few work items to fill the GPU)
  */
 #ifndef BAT_H_
 #define BAT_H_
@@ -126,6 +152,19 @@ size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
                                int32_t max_prefix_len);
 
 /*
+ * bat_attn_prefill_workspace_size -- an upper bound of
+ * bat_attn_workspace_size over both dtypes and every max_suffix_len up to
+ * total_suffix: enough workspace for any bat_attn_prefill call with these
+ * B, H, D, total_suffix and max_prefix_len.  bat_attn_workspace_size gives
+ * the exact (smaller) figure when the dtype and the suffix bound are known.
+ * Returns 0 for invalid arguments, or when the bound would need work lists
+ * of 2^30 items or more.
+ */
+size_t bat_attn_prefill_workspace_size(int32_t B, int32_t H, int32_t D,
+                                       int32_t total_suffix,
+                                       int32_t max_prefix_len);
+
+/*
  * bat_attn_prefill -- prefill attention of the suffix rows over the cached
  * prefix and their own group (the Bipartite Attention of the Bat page,
  * section "This paper's idea": either the user history or a set of cached
@@ -143,14 +182,20 @@ size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
  *                   uses it
  *   softmax_scale   multiplies q.k (pass 1/sqrt(D) for standard attention)
  *   total_suffix    host copy of cu_suffix_lens[B]
- *   max_suffix_len, max_prefix_len  host upper bounds over requests
+ *   max_suffix_len, max_prefix_len  host upper bounds over requests; every
+ *                   request must lie within them (checked under
+ *                   BAT_VALIDATE=1).  When B * max_suffix_len ==
+ *                   total_suffix (all suffixes equally long) and no prefix
+ *                   is split, the kernels place the work themselves and no
+ *                   planner launch precedes them.
  *   out             device [total_suffix, H, D], dtype dt
  *   lse             device float32 [H, total_suffix] (natural log), or NULL
- *   workspace       device, >= bat_attn_workspace_size(...) bytes
+ *   workspace       device, >= bat_attn_workspace_size(...) bytes (or
+ *                   bat_attn_prefill_workspace_size(...))
  * Supported: BAT_BF16 with D in {64, 128}; BAT_F32 with D in {32, 64, 128}.
  * Requests with no suffix tokens write nothing.  The result does not depend
- * on the physical placement of blocks: the reduction order depends only on
- * logical lengths.
+ * on the physical placement of blocks, nor on where the work runs: the
+ * reduction order of a row depends only on logical lengths.
  */
 bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                             const int32_t *cu_suffix_lens,

@@ -17,7 +17,8 @@ BAT_OK, BAT_ERR_INVALID_ARG, BAT_ERR_UNSUPPORTED, BAT_ERR_BLOCK_TABLE, BAT_ERR_W
 BAT_F32, BAT_BF16 = 0, 1
 BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 
-EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill",
+EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill_workspace_size",
+            "bat_attn_prefill",
             "bat_attn_prefix_rows", "bat_attn_item_local", "bat_attn_isolated_workspace_size",
             "bat_attn_prefill_isolated", "bat_attn_gqa_workspace_size", "bat_attn_prefill_gqa",
             "bat_lse_merge", "bat_sched_state_size", "bat_sched_init", "bat_sched_step",
@@ -61,6 +62,8 @@ def load():
     lib.bat_kv_build.restype = I
     lib.bat_attn_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.bat_attn_workspace_size.restype = ctypes.c_size_t
+    lib.bat_attn_prefill_workspace_size.argtypes = [I, I, I, I, I]
+    lib.bat_attn_prefill_workspace_size.restype = ctypes.c_size_t
     lib.bat_attn_prefill.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I, I,
                                      P, P, P, ctypes.c_size_t, P]
     lib.bat_attn_prefill.restype = I
@@ -118,6 +121,26 @@ def _torch():
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def default_scale(D) -> float:
+    """1/sqrt(D) rounded once to float32 (what the kernels receive)."""
+    import math
+    import numpy as np
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def _max_len(cu):
+    """Longest request of a cumulative-length array: a copy to the host, then numpy."""
+    import numpy as np
+    c = cu.cpu().numpy()
+    return int(np.diff(c).max()) if c.shape[0] > 1 else 0
+
+
+def _max_val(x):
+    import numpy as np
+    a = x.cpu().numpy()
+    return int(a.max()) if a.size else 0
 
 
 def _stream():
@@ -187,6 +210,11 @@ def workspace_size(B, H, D, dtype_code, total_suffix, max_suffix_len, max_prefix
                                               max_suffix_len, max_prefix_len))
 
 
+def prefill_workspace_size(B, H, D, total_suffix, max_prefix_len) -> int:
+    """The bound over both dtypes and every suffix bound up to total_suffix."""
+    return int(load().bat_attn_prefill_workspace_size(B, H, D, total_suffix, max_prefix_len))
+
+
 def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
                  user_pool=None, item_pool=None, softmax_scale=None, max_suffix_len=None,
                  max_prefix_len=None, out=None, lse=None, workspace=None, want_lse=False):
@@ -207,11 +235,11 @@ def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
     total, H, D = q.shape
     B = cu_suffix_lens.shape[0] - 1
     if max_suffix_len is None:
-        max_suffix_len = int((cu_suffix_lens[1:] - cu_suffix_lens[:-1]).max().item()) if B else 0
+        max_suffix_len = _max_len(cu_suffix_lens)
     if max_prefix_len is None:
-        max_prefix_len = int(prefix_lens.max().item()) if B else 0
+        max_prefix_len = _max_val(prefix_lens)
     if softmax_scale is None:
-        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+        softmax_scale = default_scale(D)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
@@ -253,9 +281,9 @@ def attn_prefix_rows(q, k, v, cu_prefix_lens, softmax_scale=None, max_prefix_len
     total, H, D = q.shape
     B = cu_prefix_lens.shape[0] - 1
     if max_prefix_len is None:
-        max_prefix_len = int((cu_prefix_lens[1:] - cu_prefix_lens[:-1]).max().item()) if B else 0
+        max_prefix_len = _max_len(cu_prefix_lens)
     if softmax_scale is None:
-        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+        softmax_scale = default_scale(D)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
@@ -286,7 +314,7 @@ def attn_item_local(q, k, v, tokens_per_item, softmax_scale=None, out=None, lse=
     if T <= 0 or total % T:
         raise ValueError("rows must be a whole number of items")
     if softmax_scale is None:
-        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+        softmax_scale = default_scale(D)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype)
@@ -318,11 +346,11 @@ def attn_prefill_gqa(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_ta
     H_kv = k.shape[1]
     B = cu_suffix_lens.shape[0] - 1
     if max_suffix_len is None:
-        max_suffix_len = int((cu_suffix_lens[1:] - cu_suffix_lens[:-1]).max().item()) if B else 0
+        max_suffix_len = _max_len(cu_suffix_lens)
     if max_prefix_len is None:
-        max_prefix_len = int(prefix_lens.max().item()) if B else 0
+        max_prefix_len = _max_val(prefix_lens)
     if softmax_scale is None:
-        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+        softmax_scale = default_scale(D)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
@@ -365,11 +393,11 @@ def attn_prefill_isolated(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, blo
     total, H, D = q.shape
     B = cu_suffix_lens.shape[0] - 1
     if max_suffix_len is None:
-        max_suffix_len = int((cu_suffix_lens[1:] - cu_suffix_lens[:-1]).max().item()) if B else 0
+        max_suffix_len = _max_len(cu_suffix_lens)
     if max_prefix_len is None:
-        max_prefix_len = int(prefix_lens.max().item()) if B else 0
+        max_prefix_len = _max_val(prefix_lens)
     if softmax_scale is None:
-        softmax_scale = float(torch.tensor(D, dtype=torch.float64).rsqrt().float())
+        softmax_scale = default_scale(D)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)

@@ -1,7 +1,9 @@
 // C ABI of libbat: argument validation, workspace layout, kernel dispatch.
 // Every launch goes on the caller's stream; nothing here allocates memory.
+#include <condition_variable>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -10,10 +12,10 @@ hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu, cons
                            int32_t bt_stride, int32_t B, int32_t H, int32_t D, int32_t total,
                            int elem_bytes, void *pk, void *pv, int32_t num_blocks,
                            int32_t bs_log2, int32_t *err, hipStream_t stream);
-hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B, int32_t H,
-                       int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
-                       int32_t *g_scratch, ReqMeta *meta, WorkItem *items, int32_t *hdr,
-                       hipStream_t stream);
+hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, const PlanBounds &bd,
+                       int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len,
+                       int32_t max_p, int32_t grid, int32_t *g_scratch, ReqMeta *meta,
+                       WorkItem *items, int32_t *hdr, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
                             hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
@@ -30,12 +32,50 @@ int bf16_keys_per_tile(int D);
 int f32_rows_per_item();
 int f32_keys_per_tile();
 
-// Error word of bat_kv_build under BAT_VALIDATE (one per device).
-__device__ int32_t g_kv_build_err;
+// Error words of bat_kv_build under BAT_VALIDATE: each validated call holds
+// one of them (per device) from its launch until it has read it back, so
+// validated builds on different streams or threads report only their own
+// violations.  More than kErrSlots such calls at once on one device wait.
+constexpr int kErrSlots = 64;
+constexpr int kMaxDevices = 64;
+__device__ int32_t g_kv_build_err[kErrSlots];
 
 __global__ void clear_word_kernel(int32_t *w) { *w = 0; }
 
 namespace {
+
+std::mutex g_slot_mu;
+std::condition_variable g_slot_cv;
+uint64_t g_slot_busy[kMaxDevices];
+
+// An error word of this device's array for one validated call.
+class ErrSlot {
+ public:
+  bat_status acquire() {
+    if (hipGetDevice(&dev_) != hipSuccess || dev_ < 0 || dev_ >= kMaxDevices) return BAT_ERR_HIP;
+    int32_t *base = nullptr;
+    if (hipGetSymbolAddress((void **)&base, HIP_SYMBOL(g_kv_build_err)) != hipSuccess)
+      return BAT_ERR_HIP;
+    std::unique_lock<std::mutex> lk(g_slot_mu);
+    g_slot_cv.wait(lk, [&] { return ~g_slot_busy[dev_] != 0; });
+    slot_ = __builtin_ctzll(~g_slot_busy[dev_]);
+    g_slot_busy[dev_] |= uint64_t(1) << slot_;
+    word = base + slot_;
+    return BAT_OK;
+  }
+  ~ErrSlot() {
+    if (slot_ < 0) return;
+    {
+      std::lock_guard<std::mutex> lk(g_slot_mu);
+      g_slot_busy[dev_] &= ~(uint64_t(1) << slot_);
+    }
+    g_slot_cv.notify_one();
+  }
+  int32_t *word = nullptr;
+
+ private:
+  int dev_ = -1, slot_ = -1;
+};
 
 bool validate_enabled() {
   const char *e = std::getenv("BAT_VALIDATE");
@@ -76,7 +116,8 @@ struct Plan {
 // partial (candidate-isolated suffixes); prefixes are then never split.
 // hg: query heads per key/value head (grouped heads; 1 otherwise).
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
-               int32_t max_p, Plan &pl, bool prefix_only = false, int32_t hg = 1) {
+               int32_t max_p, Plan &pl, bool prefix_only = false, int32_t hg = 1,
+               bool allow_split = true) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
@@ -99,8 +140,8 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
   const int64_t target = 512;
   pl.chunk_len = 0;
-  if (prefix_only) {
-    // one partial row per suffix row, no split
+  if (prefix_only || !allow_split) {
+    // prefix-only rows: one partial row per suffix row, no split
   } else if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v > 0) pl.chunk_len = ((v + pl.bn - 1) / pl.bn) * pl.bn;
@@ -185,10 +226,12 @@ bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
   if (!k || !v || !cu_lens || !block_table || !pool->k || !pool->v) return BAT_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   const bool val = validate_enabled();
+  ErrSlot slot;
   int32_t *err = nullptr;
   if (val) {
-    if (hipGetSymbolAddress((void **)&err, HIP_SYMBOL(g_kv_build_err)) != hipSuccess)
-      return BAT_ERR_HIP;
+    const bat_status s = slot.acquire();
+    if (s != BAT_OK) return s;
+    err = slot.word;
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, err);
   }
   const int eb = dt == BAT_BF16 ? 2 : 4;
@@ -213,6 +256,20 @@ size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
   return pl.total;
 }
 
+size_t bat_attn_prefill_workspace_size(int32_t B, int32_t H, int32_t D, int32_t total_suffix,
+                                       int32_t max_prefix_len) {
+  // the largest workspace over both dtypes, with max_suffix_len at its
+  // largest possible value (one request holding every suffix row)
+  size_t n = 0;
+  for (bat_dtype dt : {BAT_F32, BAT_BF16}) {
+    if (!supported(dt, D)) continue;
+    Plan pl;
+    if (!make_plan(B, H, D, dt, total_suffix, total_suffix, max_prefix_len, pl)) return 0;
+    if (pl.total > n) n = pl.total;
+  }
+  return n;
+}
+
 }  // extern "C"
 
 namespace bat {
@@ -229,7 +286,7 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
                      int32_t max_prefix_len, void *out, float *lse, void *workspace,
                      size_t workspace_bytes, void *stream, bool prefix_only = false,
                      const float **part_o = nullptr, const float **part_lse = nullptr,
-                     int32_t H_kv = 0, bool *self_key = nullptr) {
+                     int32_t H_kv = 0, bool *self_key = nullptr, bool allow_split = true) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -241,7 +298,8 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
     return BAT_ERR_INVALID_ARG;
   const int32_t hg = H_kv > 0 ? H / H_kv : 1;
   Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only, hg))
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only, hg,
+                 allow_split))
     return BAT_ERR_INVALID_ARG;
   if (!workspace) return BAT_ERR_WORKSPACE;
   if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
@@ -282,11 +340,25 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   p.part_lse = (float *)(ws + pl.off_part_lse);
 
   hipStream_t st = (hipStream_t)stream;
-  if (launch_plan(cu_suffix_lens, prefix_lens, B, H, hg, pl.bm, pl.chunk_len, max_prefix_len,
-                  (int32_t)pl.grid, (int32_t *)(ws + pl.off_scratch),
-                  (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
-                  st) != hipSuccess)
-    return BAT_ERR_HIP;
+  // A batch whose suffixes all have max_suffix_len rows (the bound is tight
+  // and sums to total_suffix) and whose prefixes are never split needs no
+  // planner launch: the kernels compute the same placement from their
+  // workgroup index.  Under validation the planner always runs (it checks
+  // the lengths).
+  const int64_t t_rows = ((int64_t)max_suffix_len + pl.bm - 1) / pl.bm;
+  if (!val && pl.max_chunks == 1 && (int64_t)B * max_suffix_len == total_suffix) {
+    p.an_rows = (int32_t)t_rows;
+    p.an_groups = B * p.H_kv;
+    p.an_hg = hg;
+  } else {
+    PlanBounds bd{max_suffix_len, total_suffix, prefix_mode, bt_stride, p.pool_bs_log2[0],
+                  p.pool_bs_log2[1]};
+    if (launch_plan(cu_suffix_lens, prefix_lens, bd, B, H, hg, pl.bm, pl.chunk_len,
+                    max_prefix_len, (int32_t)pl.grid, (int32_t *)(ws + pl.off_scratch),
+                    (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
+                    st) != hipSuccess)
+      return BAT_ERR_HIP;
+  }
   const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, pl.flat_gather, (int)pl.grid, st)
                                       : launch_attn_f32(p, D, (int)pl.grid, st);
   if (e != hipSuccess) return BAT_ERR_HIP;

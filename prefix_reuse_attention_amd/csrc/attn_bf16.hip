@@ -616,7 +616,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st1k[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1v[C::TILE];
 
-  const WorkItem it = p.items[blockIdx.x];
+  const WorkItem it = work_item(p, blockIdx.x);
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
   const ItemRange x = item_range(p, it);
   const int head = it.h;
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t v1[C::TILE];
   __shared__ u32x4 s_tab[TC::kTabTiles];
 
-  const WorkItem it = p.items[blockIdx.x];
+  const WorkItem it = work_item(p, blockIdx.x);
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
   const ItemRange x = item_range(p, it);
   const int head = it.h;

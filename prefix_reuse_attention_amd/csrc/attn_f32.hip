@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float Ks[kF32Keys * KROW];
   __shared__ __attribute__((aligned(16))) float Vs[kF32Keys * KROW];
 
-  const WorkItem it = p.items[blockIdx.x];
+  const WorkItem it = work_item(p, blockIdx.x);
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
   const ItemRange x = item_range(p, it);
   const int head = it.h;

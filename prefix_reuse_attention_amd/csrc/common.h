@@ -39,6 +39,15 @@ struct ReqMeta {
   int32_t part_off;   // first partial row of this request (split only)
 };
 
+// What the planner checks the per-request lengths against (reported in the
+// workspace header's error word; the host reads it under validation).
+struct PlanBounds {
+  int32_t max_s, total_s;        // suffix bound and cu_s[B]
+  const uint8_t *prefix_mode;    // [B] or null (all user mode)
+  int32_t bt_stride;             // block-table entries per request
+  int32_t lg_user, lg_item;      // log2 of each pool's block size
+};
+
 // Everything the attention kernels read, passed by value.
 struct AttnParams {
   const void *q, *k, *v;          // packed suffix [total_s, H, D]
@@ -62,7 +71,13 @@ struct AttnParams {
   int32_t self_key;               // with prefix_only: each row also sees its own suffix
                                   // token (single-token candidates), and the kernel writes
                                   // the final row to out / lse (bf16 kernels only)
-  int32_t max_prefix;             // host bound; longer prefixes are clamped to it
+  int32_t max_prefix;             // host bound; longer prefixes are clamped to it (and
+                                  // reported by the planner under validation)
+  // Work list: the planner's items (an_rows == 0), or, for a batch whose
+  // suffixes all have the same length and whose prefixes are not split, the
+  // same placement computed from the workgroup index (an_rows row tiles per
+  // request and query head, an_groups = B * H_kv groups of an_hg query heads)
+  int32_t an_rows, an_groups, an_hg;
   const WorkItem *items;
   const ReqMeta *meta;
   int32_t *err;                   // workspace header error word, or null
@@ -80,6 +95,22 @@ struct ItemRange {
   bool partial;  // write an fp32 partial (split chunk, or prefix-only rows)
 };
 
+// The work item of workgroup `bid`.  Group g (request g / H_kv, key/value
+// head g % H_kv) goes to XCD g % 8 (workgroups are dealt to the XCDs
+// round-robin by index) and takes consecutive slots there: its an_hg query
+// heads, each with its an_rows row tiles.  This is the planner's placement
+// for such a batch, less its longest-first order (all suffixes are equal).
+__device__ inline WorkItem work_item(const AttnParams &p, int bid) {
+  if (p.an_rows == 0) return p.items[bid];
+  const int x = bid % kNumXcd, s = bid / kNumXcd;
+  const int T = p.an_hg * p.an_rows;  // items per group
+  const int j = s / T, t = s - j * T;
+  const int g = x + kNumXcd * j;
+  if (g >= p.an_groups) return WorkItem{-1, 0, 0, 0};
+  const int r = g / p.H_kv, hk = g - r * p.H_kv;
+  return WorkItem{r, hk * p.an_hg + t / p.an_rows, t % p.an_rows, 0};
+}
+
 __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) {
   ItemRange x;
   x.q0 = p.cu_s[it.r];
@@ -87,7 +118,7 @@ __device__ inline ItemRange item_range(const AttnParams &p, const WorkItem &it) 
   // no prefix arrays (prefix-row attention): every request has an empty prefix
   x.n_p = p.prefix_lens ? min(max(p.prefix_lens[it.r], 0), p.max_prefix) : 0;
   x.mode = p.prefix_mode && p.prefix_mode[it.r] ? 1 : 0;
-  const ReqMeta m = p.meta[it.r];
+  const ReqMeta m = p.an_rows ? ReqMeta{1, 0} : p.meta[it.r];
   x.n_chunks = m.n_chunks;
   x.part_off = m.part_off;
   if (x.n_chunks <= 1) {

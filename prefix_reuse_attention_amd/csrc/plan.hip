@@ -70,6 +70,7 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 template <typename ReqPtr>
 __device__ __forceinline__ void plan_body(
     const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
+    const PlanBounds &bd,
     int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
     ReqPtr req, int32_t stride, int32_t (*s_wave)[kNumXcd], int32_t *s_total,
     __attribute__((address_space(3))) int32_t *fast, ReqMeta *__restrict__ meta,
@@ -104,6 +105,16 @@ __device__ __forceinline__ void plan_body(
       const int nc = req_nc[r], n_s = req_ns[r];
       meta[r] = ReqMeta{nc, part[0]};
       if (nc > 1 && n_s > 0) part[0] += nc * n_s;
+      // lengths against the caller's bounds and table (past the scan's
+      // barrier, so after the header was cleared): reported, while the
+      // kernels clamp a prefix to max_p and skip rows past total_s
+      bool bad = n_s < 0 || n_s > bd.max_s || cu_s[r] < 0 || cu_s[r + 1] > bd.total_s;
+      if (prefix_lens) {
+        const int np = prefix_lens[r];
+        const int lg = (bd.prefix_mode && bd.prefix_mode[r]) ? bd.lg_item : bd.lg_user;
+        bad |= np < 0 || np > max_p || (np > 0 && ((np - 1) >> lg) >= bd.bt_stride);
+      }
+      if (bad) atomicOr(&hdr[kHdrError], kErrLength);
     }
   }
   __syncthreads();
@@ -225,7 +236,7 @@ __device__ __forceinline__ void plan_body(
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens,
+    const int32_t *__restrict__ cu_s, const int32_t *__restrict__ prefix_lens, PlanBounds bd,
     int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p, int32_t grid,
     int32_t *__restrict__ g_scratch,  // [4 * B] used when B > kPlanLds
     ReqMeta *__restrict__ meta, WorkItem *__restrict__ items, int32_t *hdr) {
@@ -234,18 +245,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ int32_t s_req[4 * kPlanLds];
   __shared__ int32_t s_fast[(kNumXcd + 4) * kPlanThreads];
   if (B <= kPlanLds)
-    plan_body(cu_s, prefix_lens, B, H, hg, bm, chunk_len, max_p, grid, (lds_i32 *)s_req, kPlanLds,
+    plan_body(cu_s, prefix_lens, bd, B, H, hg, bm, chunk_len, max_p, grid, (lds_i32 *)s_req,
+              kPlanLds,
               s_wave, s_total, (lds_i32 *)s_fast, meta, items, hdr);
   else
-    plan_body(cu_s, prefix_lens, B, H, hg, bm, chunk_len, max_p, grid, g_scratch, B, s_wave,
+    plan_body(cu_s, prefix_lens, bd, B, H, hg, bm, chunk_len, max_p, grid, g_scratch, B, s_wave,
               s_total, (lds_i32 *)s_fast, meta, items, hdr);
 }
 
-hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
-                       int32_t H, int32_t hg, int32_t bm, int32_t chunk_len, int32_t max_p,
-                       int32_t grid, int32_t *g_scratch, ReqMeta *meta, WorkItem *items,
-                       int32_t *hdr, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_s, prefix_lens,
+hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, const PlanBounds &bd,
+                       int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len,
+                       int32_t max_p, int32_t grid, int32_t *g_scratch, ReqMeta *meta,
+                       WorkItem *items, int32_t *hdr, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_s, prefix_lens, bd,
                      B, H, hg, bm, chunk_len, max_p, grid, g_scratch, meta, items, hdr);
   return hipGetLastError();
 }

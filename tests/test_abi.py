@@ -137,6 +137,28 @@ def test_workspace_size(lib):
     assert f(1, 2, 128, api.BAT_BF16, 64, 64, 16384) > f(1, 2, 128, api.BAT_BF16, 64, 64, 1024)
 
 
+def test_prefill_workspace_size_bounds_every_call(lib):
+    """The bound with the surveyed signature (no dtype, no suffix bound)
+    covers the exact size for both dtypes and every suffix bound up to
+    total_suffix, and is rejected where the exact size is."""
+    f, g = lib.bat_attn_prefill_workspace_size, lib.bat_attn_workspace_size
+    for B, H, D, total, max_p in [(2, 8, 128, 1024, 1024), (16, 16, 128, 8192, 8192),
+                                  (1, 2, 64, 64, 16384), (32, 8, 64, 8192, 1024),
+                                  (128, 8, 128, 70000, 16384), (3, 4, 32, 24, 64)]:
+        bound = f(B, H, D, total, max_p)
+        assert bound > 0
+        for dt in (api.BAT_F32, api.BAT_BF16):
+            for max_s in sorted({1, total // B, total // 2, total}):
+                n = g(B, H, D, dt, total, max_s, max_p)
+                if n:
+                    assert n <= bound, (B, H, D, dt, total, max_s, max_p)
+    assert f(2, 8, 96, 1024, 1024) == 0
+    assert f(-1, 8, 128, 1024, 1024) == 0
+    assert f(2, 0, 128, 1024, 1024) == 0
+    # head dim 32 has only the fp32 kernel: the bound is the fp32 size
+    assert f(1, 4, 32, 8, 64) == max(g(1, 4, 32, api.BAT_F32, 8, s, 64) for s in range(1, 9))
+
+
 def prefix_rows(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cu=FAKE, B=2, H=8, D=128, dt=api.BAT_BF16, scale=0.088,
              total=1024, max_p=512, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None)

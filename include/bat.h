@@ -211,6 +211,40 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                             void *stream);
 
 /*
+ * bat_attn_prefill_noalloc -- bat_attn_prefill with no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, semantics, dtypes and head dims as bat_attn_prefill; the work
+ * list and any split-prefix partials live in a device array inside the
+ * library (bat_attn_noalloc_scratch_bytes() bytes, 32 MiB; one copy per
+ * GPU, held until the process ends; its address is looked up on the first
+ * call on each device).  The call allocates nothing.  When bat_attn_prefill
+ * would split the prefixes and the partials do not fit, the rows are
+ * computed unsplit (the same rows up to rounding); a batch whose unsplit
+ * work list does not fit returns BAT_ERR_WORKSPACE.  Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other threads) race and must not be issued.
+ */
+bat_status bat_attn_prefill_noalloc(const void *q, const void *k,
+                                    const void *v,
+                                    const int32_t *cu_suffix_lens,
+                                    const int32_t *prefix_lens,
+                                    const uint8_t *prefix_mode,
+                                    const int32_t *block_table,
+                                    int32_t bt_stride,
+                                    const bat_kv_pool *user_pool,
+                                    const bat_kv_pool *item_pool, int32_t B,
+                                    int32_t H, int32_t D, bat_dtype dt,
+                                    float softmax_scale, int32_t total_suffix,
+                                    int32_t max_suffix_len,
+                                    int32_t max_prefix_len, void *out,
+                                    float *lse, void *stream);
+
+/* Bytes of the device array bat_attn_prefill_noalloc works in. */
+size_t bat_attn_noalloc_scratch_bytes(void);
+
+/*
  * bat_attn_prefix_rows -- attention of the prefix rows over their prefix.
  *
  * The prefix rows of the bipartite mask: a prefix token sees every token of

@@ -18,7 +18,7 @@ BAT_F32, BAT_BF16 = 0, 1
 BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 
 EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill_workspace_size",
-            "bat_attn_prefill",
+            "bat_attn_prefill", "bat_attn_prefill_noalloc", "bat_attn_noalloc_scratch_bytes",
             "bat_attn_prefix_rows", "bat_attn_item_local", "bat_attn_isolated_workspace_size",
             "bat_attn_prefill_isolated", "bat_attn_gqa_workspace_size", "bat_attn_prefill_gqa",
             "bat_lse_merge", "bat_sched_state_size", "bat_sched_init", "bat_sched_step",
@@ -67,6 +67,11 @@ def load():
     lib.bat_attn_prefill.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I, I,
                                      P, P, P, ctypes.c_size_t, P]
     lib.bat_attn_prefill.restype = I
+    lib.bat_attn_prefill_noalloc.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I,
+                                             I, P, P, P]
+    lib.bat_attn_prefill_noalloc.restype = I
+    lib.bat_attn_noalloc_scratch_bytes.argtypes = []
+    lib.bat_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.bat_attn_prefix_rows.argtypes = [P, P, P, P, I, I, I, I, F, I, I, P, P, P,
                                          ctypes.c_size_t, P]
     lib.bat_attn_prefix_rows.restype = I
@@ -266,6 +271,41 @@ def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "bat_attn_prefill")
     return out, lse
+
+
+def attn_prefill_noalloc(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
+                         user_pool, item_pool, softmax_scale, max_suffix_len, max_prefix_len,
+                         out, lse=None):
+    """bat_attn_prefill_noalloc: attn_prefill with no workspace; the library
+    works in its own device array.  Nothing is allocated here either: out
+    (and lse, if wanted) are the caller's, and every bound is passed in."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype)
+    _need(cu_suffix_lens, "cu_suffix_lens", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    _need(prefix_mode, "prefix_mode", torch.uint8)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    total, H, D = q.shape
+    B = cu_suffix_lens.shape[0] - 1
+    up = user_pool.struct() if user_pool is not None else None
+    ip = item_pool.struct() if item_pool is not None else None
+    st = load().bat_attn_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_suffix_lens), _ptr(prefix_lens), _ptr(prefix_mode),
+        _ptr(block_table), 0 if block_table is None else block_table.shape[1],
+        ctypes.byref(up) if up is not None else None,
+        ctypes.byref(ip) if ip is not None else None,
+        B, H, D, _dtype_code(q), float(softmax_scale), total, int(max_suffix_len),
+        int(max_prefix_len), _ptr(out), _ptr(lse), _stream())
+    _check(st, "bat_attn_prefill_noalloc")
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().bat_attn_noalloc_scratch_bytes())
 
 
 def attn_prefix_rows(q, k, v, cu_prefix_lens, softmax_scale=None, max_prefix_len=None,

@@ -403,6 +403,83 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                    max_prefix_len, out, lse, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of bat_attn_prefill_noalloc: a file-scope device array (one copy
+// per GPU, held until the process ends) in place of the caller's workspace.
+// Host code never passes the array's name to a kernel or a copy: its device
+// address on each GPU comes from hipGetSymbolAddress, taken once per device
+// on the first call there, with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace bat {
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+bat_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BAT_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BAT_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BAT_OK;
+}
+}  // namespace
+}  // namespace bat
+
+extern "C" {
+
+size_t bat_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+bat_status bat_attn_prefill_noalloc(const void *q, const void *k, const void *v,
+                                    const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                                    const uint8_t *prefix_mode, const int32_t *block_table,
+                                    int32_t bt_stride, const bat_kv_pool *user_pool,
+                                    const bat_kv_pool *item_pool, int32_t B, int32_t H,
+                                    int32_t D, bat_dtype dt, float softmax_scale,
+                                    int32_t total_suffix, int32_t max_suffix_len,
+                                    int32_t max_prefix_len, void *out, float *lse,
+                                    void *stream) {
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
+      bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(dt, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  // the plan bat_attn_prefill would take; when its split partials do not
+  // fit the scratch, the same call unsplit (the rows are the same up to
+  // rounding); beyond that, the batch is too large for this entry point
+  Plan pl;
+  bool allow_split = true;
+  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl))
+    return BAT_ERR_INVALID_ARG;
+  if (pl.total > kNoAllocScratchBytes) {
+    allow_split = false;
+    if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, false, 1,
+                   false) ||
+        pl.total > kNoAllocScratchBytes)
+      return BAT_ERR_WORKSPACE;
+  }
+  void *ws = nullptr;
+  const bat_status s = scratch_of_current_device(&ws);
+  if (s != BAT_OK) return s;
+  return attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table, bt_stride,
+                   user_pool, item_pool, B, H, D, dt, softmax_scale, total_suffix, max_suffix_len,
+                   max_prefix_len, out, lse, ws, kNoAllocScratchBytes, stream, false, nullptr,
+                   nullptr, 0, nullptr, allow_split);
+}
+
 bat_status bat_attn_prefix_rows(const void *q, const void *k, const void *v,
                                 const int32_t *cu_prefix_lens, int32_t B, int32_t H, int32_t D,
                                 bat_dtype dt, float softmax_scale, int32_t total_prefix,

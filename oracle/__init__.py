@@ -299,3 +299,114 @@ def lse_merge(parts):
         w = np.where(np.isneginf(l), 0.0, np.exp(np.asarray(l) - np.where(np.isneginf(lse), 0.0, lse)))
         out = out + w[..., None] * np.asarray(o, np.float64)
     return out, lse
+
+
+# ------------------------------------------------------------- fp8 key/value pool
+#
+# Reading taken (the pages do not describe a compressed cache; an fp8 pool
+# only trades precision for pool capacity, which the Bat page's "What it
+# costs" counts against item caches): each block of a prefix's keys (and,
+# separately, values), per head, is stored as OCP FP8 E4M3 codes with one
+# power-of-two scale 2^e per (block, head), e being the smallest integer with
+# amax <= 448 * 2^e (amax: the block's largest magnitude; e = 0 for an all-zero
+# block).  A value x is stored as the E4M3 code nearest to x / 2^e (ties to the
+# even code, sign kept) and read back as code value * 2^e.  The attention over
+# such a pool is the plain attention above with the prefix keys/values
+# replaced by their read-back values.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values():
+    """The finite non-negative values of OCP FP8 E4M3, indexed by code
+    0x00 .. 0x7E: exponent field E (4 bits, bias 7) and mantissa M (3 bits);
+    E = 0 holds M * 2^-9, E >= 1 holds 2^(E - 7) * (1 + M / 8).  Code 0x7F
+    is NaN and has no value."""
+    vals = []
+    for code in range(0x7F):
+        E, M = code >> 3, code & 7
+        vals.append(M * 2.0 ** -9 if E == 0 else 2.0 ** (E - 7) * (1 + M / 8))
+    return np.array(vals)
+
+
+def e4m3_decode(codes):
+    """float64 values of uint8 E4M3 codes (sign bit 0x80; 0x7F and 0xFF are NaN)."""
+    codes = np.asarray(codes, np.uint8)
+    mag = np.append(e4m3_values(), np.nan)[codes & 0x7F]
+    return np.where(codes & 0x80, -mag, mag)
+
+
+def e4m3_encode(y):
+    """uint8 E4M3 codes of float64 values |y| <= 448: the nearest finite
+    magnitude, ties to the even code; the sign bit is the sign of y."""
+    y = np.asarray(y, np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("E4M3 holds magnitudes up to 448")
+    table = e4m3_values()
+    hi = np.minimum(np.searchsorted(table, a), len(table) - 1)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    code = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(table[hi] == a, hi, code)                    # exact hits
+    return (code | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def fp8_scale_exponent(amax):
+    """The smallest integer e with amax <= 448 * 2^e (0 for amax = 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = math.frexp(amax)[1] - 9          # 2^(e+9) > amax >= 448 * 2^(e-1) fails below
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def fp8_quantize_blocks(x, cu_lens, block_size):
+    """Per request r, per block j of its tokens (tokens j*bs .. of the
+    request, the last block possibly partial) and per head: the scale
+    exponent of the block and its tokens' E4M3 codes.  x is packed
+    [tokens, H, D] (bf16 bits, float32 or float64).  Returns (codes
+    [tokens, H, D] uint8, exps: list over requests of [blocks, H] int,
+    read-back values [tokens, H, D] float64)."""
+    xv = _widen(x)
+    cu = np.asarray(cu_lens, np.int64)
+    codes = np.zeros(xv.shape, np.uint8)
+    back = np.zeros(xv.shape, np.float64)
+    exps = []
+    H = xv.shape[1]
+    for r in range(len(cu) - 1):
+        n = int(cu[r + 1] - cu[r])
+        nb = -(-n // block_size)
+        er = np.zeros((nb, H), np.int64)
+        for j in range(nb):
+            t0 = int(cu[r]) + j * block_size
+            t1 = int(cu[r]) + min(n, (j + 1) * block_size)
+            for h in range(H):
+                blk = xv[t0:t1, h]
+                e = fp8_scale_exponent(np.abs(blk).max())
+                er[j, h] = e
+                c = e4m3_encode(blk / 2.0 ** e)
+                codes[t0:t1, h] = c
+                back[t0:t1, h] = e4m3_decode(c) * 2.0 ** e
+        exps.append(er)
+    return codes, exps, back
+
+
+def kv_scatter_fp8(x, cu_lens, block_table, num_blocks, block_size, fill_code, fill_scale):
+    """The fp8 pool the fp8 prefix build must produce: the codes laid out as
+    kv_scatter lays out values ([num_blocks, H, block_size, D], untouched
+    slots keep fill_code) and the scales 2^e at [block_table[r][j], h]
+    (untouched blocks keep fill_scale)."""
+    codes, exps, _ = fp8_quantize_blocks(x, cu_lens, block_size)
+    pool = kv_scatter(codes, cu_lens, block_table, num_blocks, block_size, fill_code)
+    H = codes.shape[1]
+    scales = np.full((num_blocks, H), fill_scale, np.float64)
+    bt = np.asarray(block_table)
+    for r, er in enumerate(exps):
+        for j in range(er.shape[0]):
+            scales[int(bt[r, j])] = 2.0 ** er[j]
+    return pool, scales

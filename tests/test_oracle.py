@@ -637,3 +637,110 @@ def test_gqa_brute_force_head_mapping():
                              np.array([True] * n_p + [False] * n_s), scale)
         np.testing.assert_allclose(out[:, h], bo[n_p:], rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse[h], bl[n_p:], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------- fp8 key/value pool
+def test_e4m3_values_worked_and_library():
+    """The E4M3 value table: values worked by hand, and torch's float8_e4m3fn
+    reading of every code (a library decoder)."""
+    import torch
+    v = oracle.e4m3_values()
+    assert len(v) == 127 and np.all(np.diff(v) > 0)
+    for code, want in [(0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+                       (0x38, 1.0), (0x39, 1.125), (0x40, 2.0), (0x7E, 448.0)]:
+        assert v[code] == want, hex(code)
+    codes = torch.arange(0, 256, dtype=torch.int32).to(torch.uint8)
+    lib = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = oracle.e4m3_decode(np.arange(256))
+    finite = (np.arange(256) & 0x7F) != 0x7F
+    np.testing.assert_array_equal(mine[finite], lib[finite])
+
+
+def test_e4m3_encode_against_library_and_ties():
+    """Nearest code with ties to the even code, against torch's conversion
+    (round to nearest even) on float32 values, on every exact value, and on
+    every midpoint between neighbours."""
+    import torch
+    rng = np.random.default_rng(51)
+    y = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 0.01, 20000),
+                        rng.normal(0, 1e-3, 5000)]).astype(np.float32)
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(y.astype(np.float64)), lib)
+    v = oracle.e4m3_values()
+    np.testing.assert_array_equal(oracle.e4m3_encode(v), np.arange(127))
+    np.testing.assert_array_equal(oracle.e4m3_encode(-v[1:]), np.arange(1, 127) | 0x80)
+    mid = (v[:-1] + v[1:]) / 2
+    want = np.where(np.arange(126) % 2 == 0, np.arange(126), np.arange(1, 127))
+    np.testing.assert_array_equal(oracle.e4m3_encode(mid), want)
+    with pytest.raises(ValueError):
+        oracle.e4m3_encode([449.0])
+
+
+def test_fp8_scale_exponent_closed_forms():
+    assert oracle.fp8_scale_exponent(0.0) == 0
+    for k in range(-20, 21):
+        a = 448.0 * 2.0 ** k
+        assert oracle.fp8_scale_exponent(a) == k
+        assert oracle.fp8_scale_exponent(a * (1 + 2 ** -20)) == k + 1
+        assert oracle.fp8_scale_exponent(a * (1 - 2 ** -20)) == k
+    assert oracle.fp8_scale_exponent(100.0) == -2
+
+
+def test_hand_fp8_block():
+    g = json.load(open(os.path.join(GOLDEN, "hand_fp8_block.json")))
+    x = np.array(g["x"]).reshape(4, 1, 1)
+    codes, exps, back = oracle.fp8_quantize_blocks(x, [0, 4], 4)
+    assert exps[0].tolist() == [[g["exponent"]]]
+    np.testing.assert_array_equal(codes[:, 0, 0], g["codes"])
+    np.testing.assert_array_equal(back[:, 0, 0], g["read_back"])
+
+
+def test_fp8_blocks_per_block_scale_and_round_trip_bound():
+    """Blocks of one request at very different magnitudes each get their own
+    scale; every read-back value is within half an E4M3 step (at the block's
+    scale) of the stored one."""
+    rng = np.random.default_rng(52)
+    H, D, bs = 2, 8, 4
+    lens = [10, 3, 4]
+    x = rng.standard_normal((sum(lens), H, D))
+    x[4:8] *= 1e4                      # request 0, block 1
+    x[8:10] *= 1e-3                    # request 0, block 2 (partial)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    codes, exps, back = oracle.fp8_quantize_blocks(x, cu, bs)
+    assert [e.shape for e in exps] == [(3, H), (1, H), (1, H)]
+    for r in range(len(lens)):
+        for j in range(exps[r].shape[0]):
+            t0, t1 = cu[r] + j * bs, min(cu[r + 1], cu[r] + (j + 1) * bs)
+            for h in range(H):
+                e = exps[r][j, h]
+                blk = x[t0:t1, h]
+                assert np.abs(blk).max() <= 448 * 2.0 ** e < 2 * np.abs(blk).max()
+                y = np.abs(blk) / 2.0 ** e
+                step = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 1e-300))) - 3),
+                                2.0 ** -9) * 2.0 ** e
+                assert np.all(np.abs(back[t0:t1, h] - blk) <= step / 2)
+    rel = np.abs(back[8:10] - x[8:10]) / np.abs(x[8:10])
+    assert np.median(rel) < 0.05       # the small block kept its precision
+
+
+def test_kv_scatter_fp8_layout():
+    """The fp8 pool holds each request's codes where kv_scatter puts values,
+    and each (block, head) scale at the block its table row names."""
+    rng = np.random.default_rng(53)
+    H, D, bs, nb = 2, 4, 4, 7
+    lens = [6, 4]
+    x = rng.standard_normal((10, H, D))
+    cu = np.array([0, 6, 10])
+    bt = np.array([[5, 2], [0, -1]])
+    pool, scales = oracle.kv_scatter_fp8(x, cu, bt, nb, bs, 0xFF, -1.0)
+    codes, exps, back = oracle.fp8_quantize_blocks(x, cu, bs)
+    np.testing.assert_array_equal(pool[5, :, :, :].transpose(1, 0, 2), codes[0:4])
+    np.testing.assert_array_equal(pool[2, :, :2, :].transpose(1, 0, 2), codes[4:6])
+    np.testing.assert_array_equal(pool[0, :, :, :].transpose(1, 0, 2), codes[6:10])
+    assert np.all(pool[2, :, 2:] == 0xFF) and np.all(pool[1] == 0xFF)
+    np.testing.assert_array_equal(scales[5], 2.0 ** exps[0][0])
+    np.testing.assert_array_equal(scales[2], 2.0 ** exps[0][1])
+    np.testing.assert_array_equal(scales[0], 2.0 ** exps[1][0])
+    assert np.all(scales[[1, 3, 4, 6]] == -1.0)
+    dec = oracle.e4m3_decode(pool[5]) * scales[5][:, None, None]
+    np.testing.assert_array_equal(dec.transpose(1, 0, 2), back[0:4])

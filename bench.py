@@ -467,59 +467,64 @@ SCHED = dict(n_requests=40000, num_users=20000, num_items=20000, items_per_reque
              budget_tokens=1 << 21, item_slots=8192, user_block=64, window=64, H=8, D=128)
 
 
-def _window_work(tr, res, lo, hi, H, D, seed):
-    """The attention work a policy's choices imply for queries lo..hi-1, on
-    the device: the prefill of every query over its prefix (user mode: the
-    m*T item tokens over the user history; item mode: the user tokens over
-    the query's items), prefix rows of the users it missed and per-item rows
-    of the items it missed.  Returns a step callable and its query-key pairs."""
+def _window_work(tr, c, policy, ucap, icap, H, D, seed):
+    """The serving step of the last `window` queries of the stream under one
+    policy, on the device: the library's scheduler serves the earlier queries
+    on the host (warm pools), then each query of the window in order, with
+    every prefix it computes written into its pool place (bat_kv_build), its
+    prefix rows computed (bat_attn_prefix_rows / bat_attn_item_local), and
+    the prefill of its suffix over its prefix read from the pools
+    (bat_attn_prefill), grouped into sub-batches (serving.Placement).  What
+    the window reads from the warm pools is written there beforehand.
+    Returns a step callable, the window's query-key pairs and its plan."""
     import numpy as np
     import torch
     from prefix_reuse_attention_amd import api
     from prefix_reuse_attention_amd import workloads as W
-    from prefix_reuse_attention_amd.device import DeviceWorkload, to_device
-    T, m = tr.item_tokens, tr.items.shape[1]
-    n_u = tr.user_len[tr.user[lo:hi]].astype(np.int32)
-    mode = res["mode"][lo:hi].astype(np.uint8)
-    item = mode == W.ITEM
-    n_s = np.where(item, n_u, m * T).astype(np.int32)
-    n_p = np.where(item, m * T, n_u).astype(np.int32)
-    wl = W.make_custom(dtype="bf16", H=H, D=D, n_s=n_s, n_p=n_p, mode=mode, seed=seed,
-                       num_items=tr.num_items, name="schedule window")
-    for r in np.nonzero(item)[0]:           # the queries' own items
-        wl.block_table[r, :m] = tr.items[lo + r]
-    dw = DeviceWorkload(wl)
-    ws = dw.workspace()
-    out = torch.empty_like(dw.q)
-    rng = np.random.default_rng(seed + 1)
-    miss_u = (~item) & (res["user_hit"][lo:hi] == 0)
-    lens = n_u[miss_u]
-    pr = None
-    if len(lens):
-        n = int(lens.sum())
-        pq, pk, pv = (to_device(W._normal(rng, (n, H, D), "bf16"), "bf16") for _ in range(3))
-        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).cuda()
-        pws = torch.empty(max(1, api.workspace_size(len(lens), H, D, api.BAT_BF16, n,
-                                                    int(lens.max()), 0)),
-                          dtype=torch.uint8, device="cuda")
-        pout = torch.empty_like(pq)
-        pr = lambda: api.attn_prefix_rows(pq, pk, pv, cu, softmax_scale=wl.scale,
-                                          max_prefix_len=int(lens.max()), out=pout, workspace=pws)
-    n_miss_items = int((m - res["item_hits"][lo:hi])[item].sum())
-    il = None
-    if n_miss_items:
-        iq, ik, iv = (to_device(W._normal(rng, (n_miss_items * T, H, D), "bf16"), "bf16")
-                      for _ in range(3))
-        iout = torch.empty_like(iq)
-        il = lambda: api.attn_item_local(iq, ik, iv, T, softmax_scale=wl.scale, out=iout)
-
-    def step():
-        if pr is not None:
-            pr()
-        if il is not None:
-            il()
-        dw.run(out=out, workspace=ws, want_lse=False)
-    return step, int(res["pairs"][lo:hi].sum())
+    from prefix_reuse_attention_amd.device import to_device
+    from prefix_reuse_attention_amd.serving import DeviceWindow, Placement
+    T, bs, B = tr.item_tokens, c["user_block"], c["window"]
+    lo = tr.R - B
+    sch = api.Scheduler(policy, T, bs, ucap, icap, tr.user_len, tr.num_items)
+    sch.step(tr.user[:lo], tr.items[:lo])
+    pl = Placement(sch, tr.user_len, T, bs, ucap, icap,
+                   transient_user_blocks=2 * (-(-int(tr.user_len.max()) // bs)),
+                   transient_item_slots=2 * tr.items.shape[1])
+    init_u, init_i = dict(pl.blocks_of), pl.slot_item.copy()
+    subs, outs = pl.plan(tr.user[lo:], tr.items[lo:], first_r=lo)
+    # what the window reads from the warm pools before writing it itself
+    written_u, written_i, pro_u, pro_i = set(), set(), {}, {}
+    for sb in subs:
+        for _, blocks in sb.user_writes:
+            written_u.update(blocks)
+        written_i.update(s for _, s in sb.item_writes)
+        for q in sb.queries:
+            if q.mode == W.USER and not written_u.intersection(q.prefix_places):
+                pro_u[q.user] = init_u[q.user]
+            elif q.mode == W.ITEM:
+                for s in q.prefix_places:
+                    if s not in written_i:
+                        pro_i[s] = int(init_i[s])
+    user_pool = api.new_pool(pl.user_pool_blocks, H, bs, D, torch.bfloat16)
+    item_pool = api.new_pool(pl.item_pool_slots, H, T, D, torch.bfloat16)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    for u, blocks in pro_u.items():
+        _, k, v = W.entity_tokens(seed, W.USER_STREAM, u, int(tr.user_len[u]), H, D)
+        api.kv_build(to_device(k, "bf16"), to_device(v, "bf16"), i32([0, len(k)]),
+                     i32([blocks]), user_pool)
+    if pro_i:
+        xs = [W.entity_tokens(seed, W.ITEM_STREAM, i, T, H, D) for i in pro_i.values()]
+        api.kv_build(to_device(np.concatenate([x[1] for x in xs]), "bf16"),
+                     to_device(np.concatenate([x[2] for x in xs]), "bf16"),
+                     i32(np.arange(0, (len(xs) + 1) * T, T)), i32([[s] for s in pro_i]),
+                     item_pool)
+    win = DeviceWindow(pl, subs, user_pool, item_pool, seed, H, D, scale)
+    pairs = int(sum(int(o["pairs"][0]) for o in outs))
+    plan = {"sub_batches": len(subs), "item_mode_queries": int(sum(int(o["mode"][0]) for o in outs)),
+            "user_writes": sum(len(sb.user_writes) for sb in subs),
+            "item_writes": sum(len(sb.item_writes) for sb in subs)}
+    return win.run, pairs, plan
 
 
 def _policy_accounting(tr, c):
@@ -585,11 +590,12 @@ def bench_schedule_workload(args):
     Host: the library's scheduler (bat_sched_*) serves the whole stream under
     the user-as-prefix policy (every token of the cache budget for users) and
     the hotness-aware one (the same budget less `item_slots` items of T
-    tokens for the item pool); the accounting of both.  Device: a window of
-    consecutive queries at the end of the stream (warm pools), with the
-    attention work each policy's choices imply run through the library's
-    kernels, timed per window.  One JSON line; `value` is queries per second
-    of the hotness-aware window's attention work."""
+    tokens for the item pool); the accounting of both.  Device: the serving
+    step of a window of consecutive queries at the end of the stream (warm
+    pools): per query the scheduler's choice, the cache writes of what it
+    computes at the places its pools give, its prefix rows and its prefill
+    over the pools, timed per window.  One JSON line; `value` is queries per
+    second of the hotness-aware window's device work."""
     import torch
     c = SCHED
     t = time.perf_counter()
@@ -608,10 +614,12 @@ def bench_schedule_workload(args):
     steps, warmup = max(1, min(args.steps, 50)), max(1, min(args.warmup, 10))
     dev = {}
     for name in pol:
-        step, pairs = _window_work(tr, res[name], lo, hi, H, D, seed=c["seed"] + 10)
+        p, ucap, icap = pol[name]
+        step, pairs, plan = _window_work(tr, c, p, ucap, icap, H, D, seed=c["seed"] + 10)
         wall_ms, kernel_ms = _timed_steps(step, steps, warmup, stream)
         dev[name] = {"ms_per_window": round(kernel_ms, 5), "wall_ms": round(wall_ms, 5),
-                     "pairs": pairs, "item_mode_queries": int(res[name]["mode"][lo:hi].sum())}
+                     "pairs": pairs, **plan}
+        assert pairs == int(res[name]["pairs"][lo:hi].sum())  # the same choices as the stream run
         print(f"[bench] window {name}: {kernel_ms:.4f} ms (events), {wall_ms:.4f} ms wall, "
               f"{pairs} pairs", file=sys.stderr, flush=True)
         del step
@@ -637,11 +645,12 @@ def bench_schedule_workload(args):
             "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel": "window: prefix rows + per-item rows + prefill",
+                         "kernel": "window: cache writes + prefix rows + per-item rows "
+                                   "+ prefill, per sub-batch",
                          "kernel_ms_mean": hk["ms_per_window"]}}
     if not args.no_cpu_baseline:
         import oracle.schedule as OS
-        n = 2000
+        n = 200
         while True:
             t = time.perf_counter()
             p, ucap, icap = pol["hotness"]

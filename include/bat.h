@@ -245,6 +245,70 @@ bat_status bat_attn_prefill_noalloc(const void *q, const void *k,
 size_t bat_attn_noalloc_scratch_bytes(void);
 
 /*
+ * An fp8 key/value pool: half the bytes of a bfloat16 pool, so twice the
+ * cached prefixes fit in the same memory (the Bat page, "What it costs
+ * (trade-offs and scope)", counts cache memory against item caches; the
+ * pages prescribe no cache format).  Each (block, head) of the keys, and of
+ * the values, holds OCP FP8 E4M3 codes and one scale 2^e, e the smallest
+ * integer with amax <= 448 * 2^e (amax: that block's largest magnitude,
+ * e = 0 for an all-zero block); a value x is the code nearest to x / 2^e
+ * (ties to the even code, sign kept) and reads back as code value * 2^e,
+ * which bfloat16 holds exactly.
+ *   k, v               device uint8 [num_blocks, H, block_size, D], codes
+ *   k_scale, v_scale   device float32 [num_blocks, H], the scales 2^e
+ * Layout and addressing otherwise as bat_kv_pool.
+ */
+typedef struct bat_kv_pool_fp8 {
+  void *k;
+  void *v;
+  float *k_scale;
+  float *v_scale;
+  int32_t num_blocks;
+  int32_t block_size;
+} bat_kv_pool_fp8;
+
+/*
+ * bat_kv_build_fp8 -- write prefix keys and values into an fp8 pool:
+ * bat_kv_build's scatter, each (request, block of its tokens, head) turned
+ * into codes with the block's own scale (a partial last block takes its
+ * amax over the tokens it holds).  Arguments as bat_kv_build; k and v are
+ * bfloat16 or float32 (dt) and D in {32, 64, 128}.  Each block must be named
+ * by one table entry only (two requests sharing a block would each write
+ * its scale).  Non-finite inputs give unspecified codes.
+ */
+bat_status bat_kv_build_fp8(const void *k, const void *v, const int32_t *cu_lens,
+                            const int32_t *block_table, int32_t bt_stride,
+                            int32_t B, int32_t H, int32_t D,
+                            int32_t total_tokens, bat_dtype dt,
+                            const bat_kv_pool_fp8 *pool, void *stream);
+
+/* Bytes of device workspace bat_attn_prefill_fp8 needs (0: invalid). */
+size_t bat_attn_fp8_workspace_size(int32_t B, int32_t H, int32_t D,
+                                   int32_t total_suffix,
+                                   int32_t max_suffix_len,
+                                   int32_t max_prefix_len);
+
+/*
+ * bat_attn_prefill_fp8 -- bat_attn_prefill over fp8 pools: the same rows,
+ * with each prefix key and value read back from its codes (code value *
+ * scale, exact in bfloat16) on the way into the attention tiles.  The suffix
+ * q, k, v and out are bfloat16 (D in {64, 128}); other arguments as
+ * bat_attn_prefill, with workspace >= bat_attn_fp8_workspace_size(...).
+ */
+bat_status bat_attn_prefill_fp8(const void *q, const void *k, const void *v,
+                                const int32_t *cu_suffix_lens,
+                                const int32_t *prefix_lens,
+                                const uint8_t *prefix_mode,
+                                const int32_t *block_table, int32_t bt_stride,
+                                const bat_kv_pool_fp8 *user_pool,
+                                const bat_kv_pool_fp8 *item_pool, int32_t B,
+                                int32_t H, int32_t D, float softmax_scale,
+                                int32_t total_suffix, int32_t max_suffix_len,
+                                int32_t max_prefix_len, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
  * bat_attn_prefix_rows -- attention of the prefix rows over their prefix.
  *
  * The prefix rows of the bipartite mask: a prefix token sees every token of
@@ -512,6 +576,13 @@ const char *bat_status_string(bat_status s);
 
 /* Library ABI version: major * 10000 + minor * 100 + patch. */
 int32_t bat_version(void);
+
+/*
+ * The name of the last HIP runtime error a library call saw in the calling
+ * thread ("hipSuccess" if none): the cause behind a BAT_ERR_HIP.  Static
+ * storage, never NULL.
+ */
+const char *bat_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -19,11 +19,12 @@ BAT_PREFIX_USER, BAT_PREFIX_ITEM = 0, 1
 
 EXPORTED = ("bat_kv_build", "bat_attn_workspace_size", "bat_attn_prefill_workspace_size",
             "bat_attn_prefill", "bat_attn_prefill_noalloc", "bat_attn_noalloc_scratch_bytes",
+            "bat_kv_build_fp8", "bat_attn_fp8_workspace_size", "bat_attn_prefill_fp8",
             "bat_attn_prefix_rows", "bat_attn_item_local", "bat_attn_isolated_workspace_size",
             "bat_attn_prefill_isolated", "bat_attn_gqa_workspace_size", "bat_attn_prefill_gqa",
             "bat_lse_merge", "bat_sched_state_size", "bat_sched_init", "bat_sched_step",
             "bat_sched_pools",
-            "bat_status_string", "bat_version")
+            "bat_status_string", "bat_version", "bat_last_hip_error")
 BAT_POLICY_USER_PREFIX, BAT_POLICY_HOTNESS = 0, 1
 
 _lib = None
@@ -32,7 +33,8 @@ _lib = None
 class BatError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        cause = f" [{load().bat_last_hip_error().decode()}]" if status == BAT_ERR_HIP else ""
+        super().__init__(f"{where}: {status_string(status)} (status {status}){cause}")
 
 
 class SchedConfig(ctypes.Structure):
@@ -47,6 +49,12 @@ class KvPool(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32)]
 
 
+class KvPoolFp8(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+
+
 def load():
     """Load libbat.so (built by prefix_reuse_attention_amd.build); raise if absent."""
     global _lib
@@ -55,6 +63,10 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"libbat.so is not built ({LIB_PATH}); run "
                            "`python -m prefix_reuse_attention_amd.build`")
+    # torch first: its HIP runtime (the one its tensors and streams belong
+    # to) is then already loaded, and libbat binds to that same copy instead
+    # of loading a second runtime of its own from the ROCm install
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     PP = ctypes.POINTER(KvPool)
@@ -70,6 +82,14 @@ def load():
     lib.bat_attn_prefill_noalloc.argtypes = [P, P, P, P, P, P, P, I, PP, PP, I, I, I, I, F, I, I,
                                              I, P, P, P]
     lib.bat_attn_prefill_noalloc.restype = I
+    P8 = ctypes.POINTER(KvPoolFp8)
+    lib.bat_kv_build_fp8.argtypes = [P, P, P, P, I, I, I, I, I, I, P8, P]
+    lib.bat_kv_build_fp8.restype = I
+    lib.bat_attn_fp8_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.bat_attn_fp8_workspace_size.restype = ctypes.c_size_t
+    lib.bat_attn_prefill_fp8.argtypes = [P, P, P, P, P, P, P, I, P8, P8, I, I, I, F, I, I, I,
+                                         P, P, P, ctypes.c_size_t, P]
+    lib.bat_attn_prefill_fp8.restype = I
     lib.bat_attn_noalloc_scratch_bytes.argtypes = []
     lib.bat_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.bat_attn_prefix_rows.argtypes = [P, P, P, P, I, I, I, I, F, I, I, P, P, P,
@@ -102,6 +122,8 @@ def load():
     lib.bat_status_string.restype = ctypes.c_char_p
     lib.bat_version.argtypes = []
     lib.bat_version.restype = I
+    lib.bat_last_hip_error.argtypes = []
+    lib.bat_last_hip_error.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -191,6 +213,102 @@ def new_pool(num_blocks, H, block_size, D, dtype, fill=None):
         k.fill_(fill)
         v.fill_(fill)
     return Pool(k, v, block_size)
+
+
+@dataclass
+class PoolFp8:
+    """An fp8 K/V pool: k and v are uint8 [num_blocks, H, block_size, D] E4M3
+    codes, k_scale and v_scale float32 [num_blocks, H] device tensors."""
+    k: object
+    v: object
+    k_scale: object
+    v_scale: object
+    block_size: int
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k.shape[0])
+
+    def struct(self):
+        return KvPoolFp8(self.k.data_ptr(), self.v.data_ptr(), self.k_scale.data_ptr(),
+                         self.v_scale.data_ptr(), self.num_blocks, self.block_size)
+
+
+def new_pool_fp8(num_blocks, H, block_size, D):
+    torch = _torch()
+    k = torch.zeros((num_blocks, H, block_size, D), dtype=torch.uint8, device="cuda")
+    return PoolFp8(k, torch.zeros_like(k),
+                   torch.zeros((num_blocks, H), dtype=torch.float32, device="cuda"),
+                   torch.zeros((num_blocks, H), dtype=torch.float32, device="cuda"), block_size)
+
+
+def kv_build_fp8(k, v, cu_lens, block_table, pool: PoolFp8):
+    """Quantise packed prefix K/V [tokens, H, D] into `pool` (E4M3 codes and
+    one power-of-two scale per block and head) through block_table."""
+    torch = _torch()
+    _need(k, "k"); _need(v, "v", k.dtype)
+    _need(cu_lens, "cu_lens", torch.int32); _need(block_table, "block_table", torch.int32)
+    for t, n in ((pool.k, "pool.k"), (pool.v, "pool.v")):
+        _need(t, n, torch.uint8)
+    for t, n in ((pool.k_scale, "pool.k_scale"), (pool.v_scale, "pool.v_scale")):
+        _need(t, n, torch.float32)
+    total, H, D = k.shape
+    B = cu_lens.shape[0] - 1
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, stride]")
+    ps = pool.struct()
+    st = load().bat_kv_build_fp8(_ptr(k), _ptr(v), _ptr(cu_lens), _ptr(block_table),
+                                 block_table.shape[1], B, H, D, total, _dtype_code(k),
+                                 ctypes.byref(ps), _stream())
+    _check(st, "bat_kv_build_fp8")
+
+
+def fp8_workspace_size(B, H, D, total_suffix, max_suffix_len, max_prefix_len) -> int:
+    return int(load().bat_attn_fp8_workspace_size(B, H, D, total_suffix, max_suffix_len,
+                                                  max_prefix_len))
+
+
+def attn_prefill_fp8(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
+                     user_pool=None, item_pool=None, softmax_scale=None, max_suffix_len=None,
+                     max_prefix_len=None, out=None, lse=None, workspace=None, want_lse=False):
+    """attn_prefill over fp8 pools (PoolFp8); q/k/v/out bfloat16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16)
+    _need(cu_suffix_lens, "cu_suffix_lens", torch.int32)
+    _need(prefix_lens, "prefix_lens", torch.int32)
+    _need(prefix_mode, "prefix_mode", torch.uint8)
+    if block_table is not None:
+        _need(block_table, "block_table", torch.int32)
+    total, H, D = q.shape
+    B = cu_suffix_lens.shape[0] - 1
+    if max_suffix_len is None:
+        max_suffix_len = _max_len(cu_suffix_lens)
+    if max_prefix_len is None:
+        max_prefix_len = _max_val(prefix_lens)
+    if softmax_scale is None:
+        softmax_scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    if workspace is None:
+        n = fp8_workspace_size(B, H, D, total, max_suffix_len, max_prefix_len)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    up = user_pool.struct() if user_pool is not None else None
+    ip = item_pool.struct() if item_pool is not None else None
+    st = load().bat_attn_prefill_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_suffix_lens), _ptr(prefix_lens), _ptr(prefix_mode),
+        _ptr(block_table), 0 if block_table is None else block_table.shape[1],
+        ctypes.byref(up) if up is not None else None,
+        ctypes.byref(ip) if ip is not None else None,
+        B, H, D, float(softmax_scale), total, int(max_suffix_len), int(max_prefix_len),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "bat_attn_prefill_fp8")
+    return out, lse
 
 
 def kv_build(k, v, cu_lens, block_table, pool: Pool):

@@ -8,10 +8,17 @@
 #include "common.h"
 
 namespace bat {
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
 hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu, const int32_t *bt,
                            int32_t bt_stride, int32_t B, int32_t H, int32_t D, int32_t total,
                            int elem_bytes, void *pk, void *pv, int32_t num_blocks,
                            int32_t bs_log2, int32_t *err, hipStream_t stream);
+hipError_t launch_kv_build_fp8(const void *k, const void *v, const int32_t *cu,
+                               const int32_t *bt, int32_t bt_stride, int32_t B, int32_t H,
+                               int32_t D, int elem_bytes, void *pk, void *pv, float *sk,
+                               float *sv, int32_t num_blocks, int32_t bs_log2, int32_t *err,
+                               hipStream_t stream);
 hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, const PlanBounds &bd,
                        int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len,
                        int32_t max_p, int32_t grid, int32_t *g_scratch, ReqMeta *meta,
@@ -52,9 +59,9 @@ uint64_t g_slot_busy[kMaxDevices];
 class ErrSlot {
  public:
   bat_status acquire() {
-    if (hipGetDevice(&dev_) != hipSuccess || dev_ < 0 || dev_ >= kMaxDevices) return BAT_ERR_HIP;
+    if (!hip_ok(hipGetDevice(&dev_)) || dev_ < 0 || dev_ >= kMaxDevices) return BAT_ERR_HIP;
     int32_t *base = nullptr;
-    if (hipGetSymbolAddress((void **)&base, HIP_SYMBOL(g_kv_build_err)) != hipSuccess)
+    if (!hip_ok(hipGetSymbolAddress((void **)&base, HIP_SYMBOL(g_kv_build_err))))
       return BAT_ERR_HIP;
     std::unique_lock<std::mutex> lk(g_slot_mu);
     g_slot_cv.wait(lk, [&] { return ~g_slot_busy[dev_] != 0; });
@@ -112,12 +119,17 @@ struct Plan {
          total = 0;
 };
 
+// The scales of fp8 pools (user, item): K and V, [blocks, H_kv] each.
+struct Fp8Scales {
+  const float *k[2], *v[2];
+};
+
 // prefix_only: the rows see their prefix only and every row gets an fp32
 // partial (candidate-isolated suffixes); prefixes are then never split.
 // hg: query heads per key/value head (grouped heads; 1 otherwise).
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
                int32_t max_p, Plan &pl, bool prefix_only = false, int32_t hg = 1,
-               bool allow_split = true) {
+               bool allow_split = true, bool fp8 = false) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
@@ -130,6 +142,9 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
     pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B && (D == 128 || max_p >= 4096))
                    ? 8 : 4;
   }
+  // fp8 pools: the four-wave kernel at head dim 128 (the eight-wave one
+  // copies every tile straight into LDS, with no place to convert codes)
+  if (fp8 && D == 128) pl.waves = 4;
   // BAT_GATHER=flat: the per-key gather of small pool blocks always takes
   // the global-load form that pools of 2 GiB or more need
   if (const char *e = std::getenv("BAT_GATHER")) pl.flat_gather = std::strcmp(e, "flat") == 0;
@@ -212,6 +227,8 @@ const char *bat_status_string(bat_status s) {
 
 int32_t bat_version(void) { return 100; }
 
+const char *bat_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
 bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
                         const int32_t *block_table, int32_t bt_stride, int32_t B, int32_t H,
                         int32_t D, int32_t total_tokens, bat_dtype dt, const bat_kv_pool *pool,
@@ -235,13 +252,13 @@ bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, err);
   }
   const int eb = dt == BAT_BF16 ? 2 : 4;
-  if (launch_kv_build(k, v, cu_lens, block_table, bt_stride, B, H, D, total_tokens, eb, pool->k,
-                      pool->v, pool->num_blocks, lg, err, st) != hipSuccess)
+  if (!hip_ok(launch_kv_build(k, v, cu_lens, block_table, bt_stride, B, H, D, total_tokens, eb, pool->k,
+                      pool->v, pool->num_blocks, lg, err, st)))
     return BAT_ERR_HIP;
   if (val) {
     int32_t h_err = 0;
-    if (hipMemcpyAsync(&h_err, err, sizeof h_err, hipMemcpyDeviceToHost, st) != hipSuccess ||
-        hipStreamSynchronize(st) != hipSuccess)
+    if (!hip_ok(hipMemcpyAsync(&h_err, err, sizeof h_err, hipMemcpyDeviceToHost, st)) ||
+        !hip_ok(hipStreamSynchronize(st)))
       return BAT_ERR_HIP;
     if (h_err) return BAT_ERR_BLOCK_TABLE;
   }
@@ -253,6 +270,54 @@ size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
                                int32_t max_prefix_len) {
   Plan pl;
   if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl)) return 0;
+  return pl.total;
+}
+
+bat_status bat_kv_build_fp8(const void *k, const void *v, const int32_t *cu_lens,
+                            const int32_t *block_table, int32_t bt_stride, int32_t B, int32_t H,
+                            int32_t D, int32_t total_tokens, bat_dtype dt,
+                            const bat_kv_pool_fp8 *pool, void *stream) {
+  if (!pool || B < 0 || H <= 0 || total_tokens < 0 || bt_stride < 0) return BAT_ERR_INVALID_ARG;
+  if (dt != BAT_F32 && dt != BAT_BF16) return BAT_ERR_INVALID_ARG;
+  if (!(D == 32 || D == 64 || D == 128)) return BAT_ERR_UNSUPPORTED;
+  const int lg = log2_exact(pool->block_size);
+  if (lg < 0 || pool->block_size > 256 || pool->num_blocks < 0) return BAT_ERR_INVALID_ARG;
+  if (total_tokens == 0) return BAT_OK;
+  if (B == 0 || bt_stride == 0) return BAT_ERR_INVALID_ARG;
+  if ((int64_t)B * bt_stride > 0x7fffffff || H > 65535) return BAT_ERR_INVALID_ARG;
+  if (!k || !v || !cu_lens || !block_table || !pool->k || !pool->v || !pool->k_scale ||
+      !pool->v_scale)
+    return BAT_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const bool val = validate_enabled();
+  ErrSlot slot;
+  int32_t *err = nullptr;
+  if (val) {
+    const bat_status s = slot.acquire();
+    if (s != BAT_OK) return s;
+    err = slot.word;
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, err);
+  }
+  if (!hip_ok(launch_kv_build_fp8(k, v, cu_lens, block_table, bt_stride, B, H, D,
+                                  dt == BAT_BF16 ? 2 : 4, pool->k, pool->v, pool->k_scale,
+                                  pool->v_scale, pool->num_blocks, lg, err, st)))
+    return BAT_ERR_HIP;
+  if (val) {
+    int32_t h_err = 0;
+    if (!hip_ok(hipMemcpyAsync(&h_err, err, sizeof h_err, hipMemcpyDeviceToHost, st)) ||
+        !hip_ok(hipStreamSynchronize(st)))
+      return BAT_ERR_HIP;
+    if (h_err) return BAT_ERR_BLOCK_TABLE;
+  }
+  return BAT_OK;
+}
+
+size_t bat_attn_fp8_workspace_size(int32_t B, int32_t H, int32_t D, int32_t total_suffix,
+                                   int32_t max_suffix_len, int32_t max_prefix_len) {
+  Plan pl;
+  if (!make_plan(B, H, D, BAT_BF16, total_suffix, max_suffix_len, max_prefix_len, pl, false, 1,
+                 true, true))
+    return 0;
   return pl.total;
 }
 
@@ -286,7 +351,8 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
                      int32_t max_prefix_len, void *out, float *lse, void *workspace,
                      size_t workspace_bytes, void *stream, bool prefix_only = false,
                      const float **part_o = nullptr, const float **part_lse = nullptr,
-                     int32_t H_kv = 0, bool *self_key = nullptr, bool allow_split = true) {
+                     int32_t H_kv = 0, bool *self_key = nullptr, bool allow_split = true,
+                     const Fp8Scales *f8 = nullptr) {
   if (max_prefix_len > 0 && (!block_table || bt_stride == 0)) return BAT_ERR_INVALID_ARG;
   AttnParams p{};
   for (int i = 0; i < 2; ++i) {
@@ -299,12 +365,19 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   const int32_t hg = H_kv > 0 ? H / H_kv : 1;
   Plan pl;
   if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only, hg,
-                 allow_split))
+                 allow_split, f8 != nullptr))
     return BAT_ERR_INVALID_ARG;
   if (!workspace) return BAT_ERR_WORKSPACE;
   if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
 
   uint8_t *ws = (uint8_t *)workspace;
+  if (f8) {
+    p.fp8 = 1;
+    for (int i = 0; i < 2; ++i) {
+      p.pool_sk[i] = f8->k[i];
+      p.pool_sv[i] = f8->v[i];
+    }
+  }
   p.prefix_only = prefix_only ? 1 : 0;
   // prefix-only rows of single-token candidates: the bf16 kernels fold each
   // row's own key into its result and write the final rows themselves
@@ -353,22 +426,21 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   } else {
     PlanBounds bd{max_suffix_len, total_suffix, prefix_mode, bt_stride, p.pool_bs_log2[0],
                   p.pool_bs_log2[1]};
-    if (launch_plan(cu_suffix_lens, prefix_lens, bd, B, H, hg, pl.bm, pl.chunk_len,
+    if (!hip_ok(launch_plan(cu_suffix_lens, prefix_lens, bd, B, H, hg, pl.bm, pl.chunk_len,
                     max_prefix_len, (int32_t)pl.grid, (int32_t *)(ws + pl.off_scratch),
                     (ReqMeta *)(ws + pl.off_meta), (WorkItem *)(ws + pl.off_items), hdr,
-                    st) != hipSuccess)
+                    st)))
       return BAT_ERR_HIP;
   }
   const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, pl.flat_gather, (int)pl.grid, st)
                                       : launch_attn_f32(p, D, (int)pl.grid, st);
-  if (e != hipSuccess) return BAT_ERR_HIP;
-  if (!prefix_only && pl.max_chunks > 1 && launch_merge_split(p, D, dt == BAT_BF16, st) != hipSuccess)
+  if (!hip_ok(e)) return BAT_ERR_HIP;
+  if (!prefix_only && pl.max_chunks > 1 && !hip_ok(launch_merge_split(p, D, dt == BAT_BF16, st)))
     return BAT_ERR_HIP;
   if (val) {
     int32_t h_err = 0;
-    if (hipMemcpyAsync(&h_err, hdr + kHdrError, sizeof h_err, hipMemcpyDeviceToHost, st) !=
-            hipSuccess ||
-        hipStreamSynchronize(st) != hipSuccess)
+    if (!hip_ok(hipMemcpyAsync(&h_err, hdr + kHdrError, sizeof h_err, hipMemcpyDeviceToHost, st)) ||
+        !hip_ok(hipStreamSynchronize(st)))
       return BAT_ERR_HIP;
     if (h_err) return BAT_ERR_BLOCK_TABLE;
   }
@@ -403,6 +475,44 @@ bat_status bat_attn_prefill(const void *q, const void *k, const void *v,
                    max_prefix_len, out, lse, workspace, workspace_bytes, stream);
 }
 
+bat_status bat_attn_prefill_fp8(const void *q, const void *k, const void *v,
+                                const int32_t *cu_suffix_lens, const int32_t *prefix_lens,
+                                const uint8_t *prefix_mode, const int32_t *block_table,
+                                int32_t bt_stride, const bat_kv_pool_fp8 *user_pool,
+                                const bat_kv_pool_fp8 *item_pool, int32_t B, int32_t H,
+                                int32_t D, float softmax_scale, int32_t total_suffix,
+                                int32_t max_suffix_len, int32_t max_prefix_len, void *out,
+                                float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (B < 0 || H <= 0 || total_suffix < 0 || max_suffix_len < 0 || max_prefix_len < 0 ||
+      bt_stride < 0)
+    return BAT_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff()) return BAT_ERR_INVALID_ARG;
+  if (!supported(BAT_BF16, D)) return BAT_ERR_UNSUPPORTED;
+  if (total_suffix == 0) return BAT_OK;  // nothing to write
+  if (B == 0 || max_suffix_len == 0) return BAT_ERR_INVALID_ARG;
+  if (!q || !k || !v || !cu_suffix_lens || !prefix_lens || !prefix_mode || !out)
+    return BAT_ERR_INVALID_ARG;
+  // the code pools travel as plain pool descriptions, their scales beside them
+  bat_kv_pool up{}, ip{};
+  Fp8Scales sc{};
+  const bat_kv_pool_fp8 *src[2] = {user_pool, item_pool};
+  bat_kv_pool *dst[2] = {&up, &ip};
+  for (int i = 0; i < 2; ++i) {
+    if (!src[i]) continue;
+    if (src[i]->num_blocks > 0 && (!src[i]->k_scale || !src[i]->v_scale))
+      return BAT_ERR_INVALID_ARG;
+    *dst[i] = bat_kv_pool{src[i]->k, src[i]->v, src[i]->num_blocks, src[i]->block_size};
+    sc.k[i] = src[i]->k_scale;
+    sc.v[i] = src[i]->v_scale;
+  }
+  return attn_rows(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table, bt_stride,
+                   user_pool ? &up : nullptr, item_pool ? &ip : nullptr, B, H, D, BAT_BF16,
+                   softmax_scale, total_suffix, max_suffix_len, max_prefix_len, out, lse,
+                   workspace, workspace_bytes, stream, false, nullptr, nullptr, 0, nullptr, true,
+                   &sc);
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
@@ -421,11 +531,11 @@ void *g_scratch_ptr[kMaxDevices];
 
 bat_status scratch_of_current_device(void **ptr) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BAT_ERR_HIP;
+  if (!hip_ok(hipGetDevice(&dev)) || dev < 0 || dev >= kMaxDevices) return BAT_ERR_HIP;
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void *p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BAT_ERR_HIP;
+    if (!hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) || !p) return BAT_ERR_HIP;
     g_scratch_ptr[dev] = p;
   }
   *ptr = g_scratch_ptr[dev];
@@ -513,8 +623,8 @@ bat_status bat_attn_item_local(const void *q, const void *k, const void *v, int3
   if (n_items == 0) return BAT_OK;
   if (!q || !k || !v || !out) return BAT_ERR_INVALID_ARG;
   const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
-  if (launch_item_local(q, k, v, n_items, T, H, D, dt == BAT_BF16, scale_log2, out, lse, nullptr,
-                        nullptr, nullptr, nullptr, 0, 0, (hipStream_t)stream) != hipSuccess)
+  if (!hip_ok(launch_item_local(q, k, v, n_items, T, H, D, dt == BAT_BF16, scale_log2, out, lse, nullptr,
+                        nullptr, nullptr, nullptr, 0, 0, (hipStream_t)stream)))
     return BAT_ERR_HIP;
   return BAT_OK;
 }
@@ -601,9 +711,9 @@ bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v
   }
   // each candidate over its own tokens, merged with its row's prefix part
   const float scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
-  if (launch_item_local(q, k, v, total_suffix / T, T, H, D, dt == BAT_BF16, scale_log2, out, lse,
+  if (!hip_ok(launch_item_local(q, k, v, total_suffix / T, T, H, D, dt == BAT_BF16, scale_log2, out, lse,
                         o_p, lse_p, cu_suffix_lens, prefix_lens, B, max_prefix_len,
-                        (hipStream_t)stream) != hipSuccess)
+                        (hipStream_t)stream)))
     return BAT_ERR_HIP;
   return BAT_OK;
 }
@@ -615,8 +725,8 @@ bat_status bat_lse_merge(const float *o_parts, const float *lse_parts, int32_t n
   if (n_parts <= 0 || rows < 0 || H <= 0 || D <= 0 || (D % 4) != 0) return BAT_ERR_INVALID_ARG;
   if (rows == 0) return BAT_OK;
   if (!o_parts || !lse_parts || !out) return BAT_ERR_INVALID_ARG;
-  if (launch_lse_merge(o_parts, lse_parts, n_parts, rows, H, D, dt == BAT_BF16, out, lse,
-                       (hipStream_t)stream) != hipSuccess)
+  if (!hip_ok(launch_lse_merge(o_parts, lse_parts, n_parts, rows, H, D, dt == BAT_BF16, out, lse,
+                       (hipStream_t)stream)))
     return BAT_ERR_HIP;
   return BAT_OK;
 }

@@ -604,7 +604,93 @@ __device__ __forceinline__ void copies_landed_barrier() {
   __syncthreads();
 }
 
-template <int D, int W, bool FLAT>
+// Prefix tiles read from an fp8 pool (E4M3 codes, one power-of-two scale per
+// block and head).  Each thread owns NP 16-byte pieces (16 codes of one key
+// row) of K and of V: during the compute of tile t it loads the pieces of
+// tile t+1 into registers with their blocks' scales (the block ids were
+// loaded during tile t-1), and after that compute it converts them --
+// code value * scale, exact in bfloat16 -- into the next LDS stage in the
+// stage's swizzled layout.  The kernel's compute is then the bfloat16 one.
+template <int D, int W>
+struct Fp8Prefix {
+  using C = Bf16Cfg<D>;
+  static constexpr int THREADS = 64 * W;
+  static constexpr int CPR8 = D / 16;         // 16-byte pieces of codes per key row
+  static constexpr int NP = C::BN * CPR8 / THREADS;
+  static_assert(NP >= 1 && NP * THREADS == C::BN * CPR8, "pieces per thread");
+  const uint8_t *pk, *pv;                     // code pools
+  const float *sk, *sv;                       // scales [blocks, H_kv]
+  const int32_t *bt_row;
+  int lg, blocks, bt_stride, H, head, p_begin, p_end;
+  int row[NP], c[NP];
+  int blk[NP];                                // block of each piece's row, next tile
+  u32x4 dk[NP], dv[NP];
+  float fk[NP], fv[NP];
+  bool bad = false;
+
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int g = tid + THREADS * j;
+      row[j] = g / CPR8;
+      c[j] = g % CPR8;
+    }
+  }
+  __device__ __forceinline__ void load_ids(int tile) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int key = p_begin + tile * C::BN + row[j];
+      const int slot = key >> lg;
+      blk[j] = (key < p_end && slot < bt_stride) ? bt_row[slot] : -1;
+    }
+  }
+  __device__ __forceinline__ void load(int tile) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int key = p_begin + tile * C::BN + row[j];
+      const bool inb = blk[j] >= 0 && blk[j] < blocks;
+      bad |= key < p_end && !inb;
+      dk[j] = dv[j] = u32x4{0u, 0u, 0u, 0u};
+      fk[j] = fv[j] = 0.f;
+      if (key < p_end && inb) {
+        const int64_t bh = (int64_t)blk[j] * H + head;
+        const int64_t off = ((bh << lg) | (key & ((1 << lg) - 1))) * D + c[j] * 16;
+        dk[j] = *(const u32x4 *)(pk + off);
+        dv[j] = *(const u32x4 *)(pv + off);
+        fk[j] = sk[bh];
+        fv[j] = sv[bh];
+      }
+    }
+  }
+  // 16 codes -> 16 bfloat16 values (two 16-byte chunks)
+  __device__ __forceinline__ static void convert(const u32x4 &d, float s, u32x4 &lo, u32x4 &hi) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[w], s, false);
+      const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[w], s, true);
+      u32x4 &dst = w < 2 ? lo : hi;
+      dst[2 * (w & 1)] = __builtin_bit_cast(uint32_t, a);
+      dst[2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, b);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t *kl, uint8_t *vl) const {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int sw = swz<D>(row[j]);
+      const int o0 = row[j] * C::RB + (((2 * c[j]) ^ sw) << 4);
+      const int o1 = row[j] * C::RB + (((2 * c[j] + 1) ^ sw) << 4);
+      u32x4 lo, hi;
+      convert(dk[j], fk[j], lo, hi);
+      *(u32x4 *)(kl + o0) = lo;
+      *(u32x4 *)(kl + o1) = hi;
+      convert(dv[j], fv[j], lo, hi);
+      *(u32x4 *)(vl + o0) = lo;
+      *(u32x4 *)(vl + o1) = hi;
+    }
+  }
+};
+
+template <int D, int W, bool FLAT, bool FP8>
 __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   using C = Bf16Cfg<D>;
   using G = WgCfg<W>;
@@ -631,7 +717,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   bf16x8 qf[C::KK];
 
   TileCopy<D, W, FLAT> cp;
-  cp.pool_k = (const uint8_t *)p.pool_k[x.mode];
+  cp.pool_k = (const uint8_t *)p.pool_k[x.mode];  // (fp8 pools: prefix tiles go through f8)
   cp.pool_v = (const uint8_t *)p.pool_v[x.mode];
   cp.ks = (const uint8_t *)p.k;
   cp.vs = (const uint8_t *)p.v;
@@ -699,8 +785,28 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   // Every copy writes its whole stage (lanes past the end of the data write
   // zeros), so the stages need no clearing.  The Q loads go out between the
   // block-id load of tile 0 and its copy, so that the latencies overlap.
-  int ids[G::CPW];
-  cp.load_ids(0, ids);
+  int ids[G::CPW];  // (fp8 pools: never read, suffix tiles plan without them)
+  // fp8 pool: the prefix tiles come through f8 (register-staged, converted
+  // to bfloat16 into the stage); suffix tiles are copied as usual
+  Fp8Prefix<D, W> f8;
+  if constexpr (FP8) {
+    f8.pk = (const uint8_t *)p.pool_k[x.mode];
+    f8.pv = (const uint8_t *)p.pool_v[x.mode];
+    f8.sk = p.pool_sk[x.mode];
+    f8.sv = p.pool_sv[x.mode];
+    f8.bt_row = cp.bt_row;
+    f8.lg = cp.lg;
+    f8.blocks = cp.blocks;
+    f8.bt_stride = p.bt_stride;
+    f8.H = p.H_kv;
+    f8.head = cp.head;
+    f8.p_begin = x.p_begin;
+    f8.p_end = x.p_end;
+    f8.init(tid);
+    f8.load_ids(0);
+  } else {
+    cp.load_ids(0, ids);
+  }
   {
     const uint16_t *q = (const uint16_t *)p.q + ((int64_t)(x.q0 + row) * p.H + head) * D;
 #pragma unroll
@@ -710,8 +816,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
       qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  cp.issue(0, ids, st0k, st0v);
-  cp.load_ids(1, ids);
+  if (FP8 && cp.n_tiles_p > 0) {
+    f8.load(0);
+    f8.load_ids(1);
+    f8.store(st0k, st0v);
+  } else {
+    cp.issue(0, ids, st0k, st0v);
+    if constexpr (!FP8) cp.load_ids(1, ids);
+  }
   copies_landed_barrier();  // tile 0 in LDS, Q in registers
 
   // Tile t is consumed from one stage while the copy of tile t+1 into the
@@ -720,11 +832,20 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   constexpr int SPACING = (C::NB * C::KK) / (2 * G::CPW);
   auto tile_step = [&](int t, uint8_t *kc, uint8_t *vc, uint8_t *kn, uint8_t *vn)
       __attribute__((always_inline)) {
-    const auto pl = cp.plan(t + 1, ids);
-    cp.load_ids(t + 2, ids);
-    compute_tile<D>(kc, vc, qf, o, sm, cs, valid_keys(t), lane, lo, [&](int i) {
-      if (i % SPACING == 0) cp.fire(pl, i / SPACING, kn, vn);
-    });
+    if (FP8 && t + 1 < cp.n_tiles_p) {
+      // the next tile is an fp8 prefix tile: its codes load during this
+      // tile's compute and are converted into the other stage after it
+      f8.load(t + 1);
+      f8.load_ids(t + 2);
+      compute_tile<D>(kc, vc, qf, o, sm, cs, valid_keys(t), lane, lo, [](int) {});
+      f8.store(kn, vn);
+    } else {
+      const auto pl = cp.plan(t + 1, ids);
+      if constexpr (!FP8) cp.load_ids(t + 2, ids);
+      compute_tile<D>(kc, vc, qf, o, sm, cs, valid_keys(t), lane, lo, [&](int i) {
+        if (i % SPACING == 0) cp.fire(pl, i / SPACING, kn, vn);
+      });
+    }
     copies_landed_barrier();  // tile t+1 landed everywhere; this stage free
   };
   for (int t = 0; t < n_tiles; t += 2) {
@@ -734,7 +855,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   }
 
   // ---- epilogue: report bad block ids, normalise, write O (and lse) or the split partial
-  if (p.err && __any(cp.bad) && lane == 0) atomicOr(p.err, kErrBlockId);
+  bool bad = cp.bad;
+  if constexpr (FP8) bad |= f8.bad;
+  if (p.err && __any(bad) && lane == 0) atomicOr(p.err, kErrBlockId);
   const float l_tot = sm.l_run + __shfl_xor(sm.l_run, 32);
   const float inv = 1.0f / l_tot;
   const float lse_nat = (sm.m_run + log2f(l_tot)) * 0.69314718055994530942f;
@@ -1166,24 +1289,32 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
 
 // Explicit instantiations of every kernel launched below (two kernel
 // templates that share device helpers otherwise lose one set of host stubs).
-template __global__ void attn_bf16_kernel<128, 4, false>(AttnParams);
-template __global__ void attn_bf16_kernel<128, 4, true>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 4, false>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 4, true>(AttnParams);
+template __global__ void attn_bf16_kernel<128, 4, false, false>(AttnParams);
+template __global__ void attn_bf16_kernel<128, 4, true, false>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 4, false, false>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 4, true, false>(AttnParams);
+template __global__ void attn_bf16_kernel<128, 4, false, true>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 4, false, true>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 8, false, true>(AttnParams);
 template __global__ void attn_bf16_pp_kernel<128, false>(AttnParams);
 template __global__ void attn_bf16_pp_kernel<128, true>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 8, false>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 8, true>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 8, false, false>(AttnParams);
+template __global__ void attn_bf16_kernel<64, 8, true, false>(AttnParams);
 
 int bf16_rows_per_item(int W) { return W == 8 ? WgCfg<8>::BM : WgCfg<4>::BM; }
 int bf16_keys_per_tile(int D) { return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN; }
 
 template <int D, int W>
 static void launch_one(const AttnParams &p, bool flat, int grid, hipStream_t stream) {
-  if (flat)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, true>), dim3(grid), dim3(64 * W), 0, stream, p);
+  if (p.fp8)  // fp8 pools are read by plain loads (no per-pool address limit)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, false, true>), dim3(grid), dim3(64 * W), 0,
+                       stream, p);
+  else if (flat)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, true, false>), dim3(grid), dim3(64 * W), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, false>), dim3(grid), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, false, false>), dim3(grid), dim3(64 * W), 0,
+                       stream, p);
 }
 
 template <int D>
@@ -1196,11 +1327,13 @@ static void launch_pp(const AttnParams &p, bool flat, int grid, hipStream_t stre
 
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
                             hipStream_t stream) {
+  clear_stale_launch_error();
   if (grid <= 0) return hipSuccess;
   bool flat = flat_gather;
   for (int m = 0; m < 2; ++m)
     flat |= (int64_t)p.pool_blocks[m] * p.H_kv * ((int64_t)2 * D << p.pool_bs_log2[m]) >
             kBufferPoolLimit;
+  if (p.fp8 && D == 128 && W != 4) return hipErrorInvalidValue;  // fp8: four waves at D=128
   if (D == 128 && W == 8)
     launch_pp<128>(p, flat, grid, stream);
   else if (D == 128 && W == 4)
@@ -1211,7 +1344,7 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
     launch_one<64, 4>(p, flat, grid, stream);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_result();
 }
 
 }  // namespace bat

@@ -130,6 +130,7 @@ int f32_rows_per_item() { return kF32Rows; }
 int f32_keys_per_tile() { return kF32Keys; }
 
 hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream) {
+  clear_stale_launch_error();
   if (grid <= 0) return hipSuccess;
   if (D == 32)
     hipLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(256), 0, stream, p);
@@ -139,7 +140,7 @@ hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t str
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_result();
 }
 
 }  // namespace bat

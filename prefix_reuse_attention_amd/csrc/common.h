@@ -59,6 +59,9 @@ struct AttnParams {
   const void *pool_v[2];
   int32_t pool_blocks[2];
   int32_t pool_bs_log2[2];
+  int32_t fp8;                    // 1: the pools hold E4M3 codes with these scales
+  const float *pool_sk[2];        // fp8: K and V scales [blocks, H_kv] per pool
+  const float *pool_sv[2];
   int32_t bt_stride;
   int32_t B, H;
   int32_t H_kv;                   // key/value heads (H for multi-head attention); query
@@ -86,6 +89,24 @@ struct AttnParams {
   float *part_o;                  // split partials [part_rows, H, D]
   float *part_lse;                // [part_rows, H]
 };
+
+// The launch helpers report the errors of their own launches: an error that
+// an earlier runtime call of the caller's thread left behind (and that the
+// caller did not collect) is cleared before the launch.
+inline void clear_stale_launch_error() { (void)hipGetLastError(); }
+
+// The last HIP error the library saw in this thread (bat_last_hip_error).
+extern thread_local hipError_t g_last_hip_error;
+inline bool hip_ok(hipError_t e) {
+  if (e == hipSuccess) return true;
+  g_last_hip_error = e;
+  return false;
+}
+inline hipError_t launch_result() {
+  const hipError_t e = hipGetLastError();
+  hip_ok(e);
+  return e;
+}
 
 // Key range of one work item: prefix keys [p_begin, p_end) and, when
 // with_suffix, the request's suffix keys.

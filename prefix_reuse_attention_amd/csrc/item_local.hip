@@ -181,6 +181,7 @@ template <int D, int T, bool BF16>
 hipError_t launch_item_local_t(const void *q, const void *k, const void *v, int32_t n_items,
                                int32_t H, float scale_log2, void *out, float *lse,
                                const PrefixPartial *pp, hipStream_t stream) {
+  clear_stale_launch_error();
   constexpr int G = D / (BF16 ? 8 : 4);
   constexpr int groups_per_block = 4 * (kWave / G);  // four waves
   const int64_t groups = (int64_t)n_items * H;
@@ -192,13 +193,14 @@ hipError_t launch_item_local_t(const void *q, const void *k, const void *v, int3
   else
     hipLaunchKernelGGL((item_local_kernel<D, T, BF16, false>), dim3((unsigned)blocks), dim3(256),
                        0, stream, q, k, v, n_items, H, scale_log2, out, lse, PrefixPartial{});
-  return hipGetLastError();
+  return launch_result();
 }
 
 template <int D, bool BF16>
 hipError_t launch_item_local_d(const void *q, const void *k, const void *v, int32_t n_items,
                                int32_t T, int32_t H, float scale_log2, void *out, float *lse,
                                const PrefixPartial *pp, hipStream_t stream) {
+  clear_stale_launch_error();
   switch (T) {
     case 1: return launch_item_local_t<D, 1, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
     case 2: return launch_item_local_t<D, 2, BF16>(q, k, v, n_items, H, scale_log2, out, lse, pp, stream);
@@ -216,6 +218,7 @@ hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_
                              void *out, float *lse, const float *o_p, const float *lse_p,
                              const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
                              int32_t max_prefix, hipStream_t stream) {
+  clear_stale_launch_error();
   const PrefixPartial part{o_p, lse_p, cu_s, prefix_lens, B, max_prefix};
   const PrefixPartial *pp = o_p ? &part : nullptr;
   if (bf16) {

@@ -62,6 +62,7 @@ hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu,
                            int32_t H, int32_t D, int32_t total, int elem_bytes,
                            void *pk, void *pv, int32_t num_blocks, int32_t bs_log2,
                            int32_t *err, hipStream_t stream) {
+  clear_stale_launch_error();
   const int64_t n_chunks = (int64_t)total * H * (D * elem_bytes / 16);
   const int threads = 256;
   int64_t blocks = (n_chunks + threads - 1) / threads;
@@ -75,7 +76,7 @@ hipError_t launch_kv_build(const void *k, const void *v, const int32_t *cu,
     hipLaunchKernelGGL(kv_build_kernel<4>, dim3((unsigned)blocks), dim3(threads), 0, stream,
                        (const uint8_t *)k, (const uint8_t *)v, cu, bt, bt_stride, B, H, D,
                        total, (uint8_t *)pk, (uint8_t *)pv, num_blocks, bs_log2, err);
-  return hipGetLastError();
+  return launch_result();
 }
 
 }  // namespace bat

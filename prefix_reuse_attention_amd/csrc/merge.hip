@@ -88,20 +88,22 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float *__restrict_
 }
 
 hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream) {
+  clear_stale_launch_error();
   const int64_t n = (int64_t)p.total_s * p.H * (D / 4);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_split_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      p, D, bf16 ? 1 : 0);
-  return hipGetLastError();
+  return launch_result();
 }
 
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
                             int H, int D, bool bf16, void *out, float *lse, hipStream_t stream) {
+  clear_stale_launch_error();
   const int64_t n = (int64_t)rows * H * (D / 4);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      o_parts, lse_parts, n_parts, rows, H, D, bf16 ? 1 : 0, out, lse);
-  return hipGetLastError();
+  return launch_result();
 }
 
 }  // namespace bat

@@ -257,9 +257,10 @@ hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, const Pl
                        int32_t B, int32_t H, int32_t hg, int32_t bm, int32_t chunk_len,
                        int32_t max_p, int32_t grid, int32_t *g_scratch, ReqMeta *meta,
                        WorkItem *items, int32_t *hdr, hipStream_t stream) {
+  clear_stale_launch_error();
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_s, prefix_lens, bd,
                      B, H, hg, bm, chunk_len, max_p, grid, g_scratch, meta, items, hdr);
-  return hipGetLastError();
+  return launch_result();
 }
 
 }  // namespace bat

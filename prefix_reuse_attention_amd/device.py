@@ -63,6 +63,29 @@ class DeviceWorkload:
             self._src["item"] = (to_device(wl.item_k, wl.dtype), to_device(wl.item_v, wl.dtype),
                                  cu, bt)
 
+    def build_pools_fp8(self):
+        """fp8 copies of the pools (E4M3 codes with a power-of-two scale per
+        block and head), built by bat_kv_build_fp8 from the same tokens and
+        block tables; they replace the bf16 pools for run_fp8."""
+        wl = self.wl
+        self.upload_prefix()
+        self.user_pool8 = self.item_pool8 = None
+        if "user" in self._src:
+            self.user_pool8 = api.new_pool_fp8(wl.user_num_blocks, wl.H, wl.user_block_size, wl.D)
+            api.kv_build_fp8(*self._src["user"], self.user_pool8)
+        if "item" in self._src:
+            self.item_pool8 = api.new_pool_fp8(wl.num_items, wl.H, W.ITEM_TOKENS, wl.D)
+            api.kv_build_fp8(*self._src["item"], self.item_pool8)
+        self.drop_prefix_source()
+
+    def run_fp8(self, out=None, lse=None, workspace=None, want_lse=True, block_table=None):
+        return api.attn_prefill_fp8(self.q, self.k, self.v, self.cu_s, self.prefix_lens,
+                                    self.prefix_mode,
+                                    self.block_table if block_table is None else block_table,
+                                    self.user_pool8, self.item_pool8, self.wl.scale, self.max_s,
+                                    self.max_p, out=out, lse=lse, workspace=workspace,
+                                    want_lse=want_lse)
+
     def alloc_pools(self, fill=None):
         wl = self.wl
         if "user" in self._src:

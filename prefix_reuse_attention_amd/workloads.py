@@ -239,6 +239,19 @@ def make_config(k: int, seed=None, materialize=True) -> Workload:
     return wl
 
 
+USER_STREAM, ITEM_STREAM = 1, 2
+
+
+def entity_tokens(seed, kind, ident, n, H, D, dtype="bf16"):
+    """(q, k, v), each [n, H, D], of one entity's tokens: user `ident`'s
+    history (kind USER_STREAM) or item `ident` (kind ITEM_STREAM).  Drawn
+    N(0, 1) from a generator seeded by (seed, kind, ident), so an entity has
+    the same tokens whichever query names it and whichever group (prefix or
+    suffix) they fall in."""
+    rng = np.random.default_rng([int(seed), int(kind), int(ident)])
+    return tuple(_normal(rng, (n, H, D), dtype) for _ in range(3))
+
+
 @dataclass
 class Traffic:
     """A seeded stream of generative-recommender queries: query r comes from

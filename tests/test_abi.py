@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -41,11 +42,26 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared_functions()) <= exported
 
 
+def test_one_hip_runtime_in_the_process():
+    """Loading the library through the binding maps exactly one HIP runtime:
+    torch's (the one its tensors and streams belong to).  A second runtime
+    loaded from the ROCm install beside torch's sees no device of its own."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from prefix_reuse_attention_amd import api\n"
+            "api.load()\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n"
+            % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "1", out.stdout + out.stderr
+
+
 def test_status_strings_and_version(lib):
     for s in range(6):
         assert api.status_string(s).startswith("BAT_")
     assert "unknown" in api.status_string(99)
     assert api.version() >= 100
+    assert lib.bat_last_hip_error() == b"hipSuccess"  # no HIP call has failed in this thread
 
 
 def _pool(num_blocks=4, block_size=64, k=FAKE, v=FAKE):

@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--workload", choices=("prefill", "isolated", "gqa", "prefix-rows",
-                                           "item-local", "schedule", "split"),
+                                           "item-local", "schedule", "split", "fp8"),
                     default="prefill",
                     help="prefill: bat_attn_prefill on --config (the default line); "
                          "isolated: bat_attn_prefill_isolated on --config with single-token "
@@ -112,7 +112,9 @@ def main():
                          "schedule: the prefix-mode choice (bat_sched_*) on Zipf traffic and "
                          "the attention work it implies for a window of queries; split: "
                          "bat_attn_prefill on 2 requests with 32768-token prefixes, which "
-                         "the planner splits into chunks merged by log-sum-exp")
+                         "the planner splits into chunks merged by log-sum-exp; fp8: "
+                         "bat_attn_prefill_fp8 on --config with the prefix pool in fp8 "
+                         "(bat_kv_build_fp8)")
     ap.add_argument("--host-sweep", action="store_true",
                     help="with --workload schedule: only the host accounting of both policies "
                          "over a grid of traffic shapes (no GPU needed)")
@@ -162,6 +164,9 @@ def main():
         return
     if args.workload in ("prefix-rows", "item-local"):
         bench_prefix_workload(args)
+        return
+    if args.workload == "fp8":
+        bench_fp8_workload(args)
         return
     isolated = args.workload == "isolated"
     gqa_heads = 0
@@ -230,24 +235,9 @@ def main():
                                  dw.block_table, dw.user_pool, dw.item_pool, wl.scale, dw.max_s,
                                  dw.max_p, out=out, lse=lse, workspace=ws)
     else:
-        def step():
-            dw.run(out=out, lse=lse, workspace=ws)
+        step = dw.prepared(out, lse, ws)  # arguments marshalled once
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall0
-    per_call_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    ms_per_step = wall_s * 1e3 / args.steps
+    ms_per_step, kernel_ms = _timed_steps(step, args.steps, args.warmup, stream)
     flops = wl.flops()
     alg_bytes = wl.alg_bytes()
     if gqa_heads:  # the work of the query heads
@@ -256,16 +246,13 @@ def main():
         flops = float(4.0 * wl.D * wl.H * np.sum(wl.n_s.astype(np.float64) * (wl.n_p + 1)))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tok_s = wl.total_s / (ms_per_step * 1e-3)
-    kernel_ms = float(per_call_ms.mean())
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     traffic = None if (isolated or gqa_heads) else measured_traffic(wl.name, 1)
     props = torch.cuda.get_device_properties(0)
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step (events: mean "
-          f"{kernel_ms:.4f}, min {per_call_ms.min():.4f}, p90 {np.percentile(per_call_ms, 90):.4f})"
-          f"; {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    print("[bench] per-call ms: " + " ".join(f"{v:.4f}" for v in per_call_ms),
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step by wall clock, "
+          f"{kernel_ms:.4f} by events on the stream; {tflops:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
     base = None
@@ -310,6 +297,71 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "cpu_baseline": base,
     }
+    print(json.dumps(line), flush=True)
+
+
+def bench_fp8_workload(args):
+    """bat_attn_prefill_fp8 on --config (default config 4) with the prefix
+    pool held in fp8 (E4M3 codes, a power-of-two scale per block and head):
+    the pool's bytes against a bfloat16 pool, the quantising build
+    (bat_kv_build_fp8, once per prefix), and the prefill's TFLOP/s."""
+    import numpy as np
+    import torch
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd import workloads as W
+    from prefix_reuse_attention_amd.device import DeviceWorkload
+    wl = W.make_config(args.config)
+    dw = DeviceWorkload(wl, build=False)
+    stream = torch.cuda.current_stream()
+    dw.build_pools_fp8()                  # first launch loads the code object: untimed
+    dw.upload_prefix()
+    src = dw._src
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    ev0.record(stream)
+    for _ in range(reps):                 # rebuilding the same pool is idempotent
+        for name, pool in (("user", dw.user_pool8), ("item", dw.item_pool8)):
+            if name in src:
+                api.kv_build_fp8(*src[name], pool)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1) / reps
+    src_bytes = dw.prefix_bytes()
+    dw.drop_prefix_source()
+    pools = [p for p in (dw.user_pool8, dw.item_pool8) if p is not None]
+    fp8_bytes = sum(p.k.numel() + p.v.numel() + 4 * (p.k_scale.numel() + p.v_scale.numel())
+                    for p in pools)
+    bf16_bytes = sum(2 * (p.k.numel() + p.v.numel()) for p in pools)
+    out = torch.empty_like(dw.q)
+    lse = torch.empty((wl.H, wl.total_s), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, api.fp8_workspace_size(wl.B, wl.H, wl.D, wl.total_s, dw.max_s,
+                                                   dw.max_p)), dtype=torch.uint8, device="cuda")
+    step = lambda: dw.run_fp8(out=out, lse=lse, workspace=ws)
+    wall_ms, kernel_ms = _timed_steps(step, args.steps, args.warmup, stream)
+    flops = wl.flops()
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    print(f"[bench] fp8 {wl.name}: {wall_ms:.4f} ms/step (events {kernel_ms:.4f}); "
+          f"{tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    line = {"workload": "fp8", "metric": "prefill attention TFLOP/s over an fp8 prefix pool, 1 GPU",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+            "dtype": "bf16 (fp8 e4m3 prefix pool)",
+            "data": "synthetic (seeded N(0,1) activations, shuffled paged prefix pool)",
+            "config": {"workload": f"{wl.name}: {wl.notes['description']}; prefix pool in fp8",
+                       "B": wl.B, "H": wl.H, "D": wl.D, "seed": wl.seed},
+            "vs_baseline": None, "alg_flops_per_step": flops,
+            "pool_bytes": {"fp8_codes_and_scales": fp8_bytes, "bf16_equivalent": bf16_bytes,
+                           "ratio": round(fp8_bytes / bf16_bytes, 4)},
+            "kv_build_fp8": {"ms": round(build_ms, 4), "bytes_read": src_bytes,
+                             "bytes_written": fp8_bytes,
+                             "GB_per_s_read_plus_write": round(
+                                 (src_bytes + fp8_bytes) / (build_ms * 1e-3) / 1e9, 1)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel": f"attn_bf16_kernel<{wl.D}, 4, false, true>",
+                         "kernel_ms_mean": round(kernel_ms, 5)}}
     print(json.dumps(line), flush=True)
 
 
@@ -365,29 +417,44 @@ def run_cpu_baseline(wl, target_s):
     print(f"[bench] oracle baseline: {len(rows)} (row, head) pairs in {dt:.1f}s",
           file=sys.stderr, flush=True)
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(), "precision": "float64",
             "sample": f"{len(rows)} random (suffix row, head) pairs of {wl.name}, float64, "
                       f"{dt:.1f} s; rate = algorithmic flops of those pairs / time",
             "suffix_tokens_per_s_equiv": round(len(rows) / wl.H / dt, 3)}
 
 
+def cpu_model():
+    """The host CPU's model name and the processors the OS shows."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical processors visible)"
+
+
 def _timed_steps(step, steps, warmup, stream):
-    import numpy as np
+    """warmup untimed steps, then exactly `steps` steps between two
+    synchronisations.  Returns (wall-clock ms per step, ms per step by two HIP
+    events on the stream the kernels run on, recorded around the timed steps
+    only: nothing else is enqueued between the steps)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         step()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    return wall_ms, float(per.mean())
+    return wall_ms, start.elapsed_time(end) / steps
 
 
 def bench_prefix_workload(args):
@@ -661,7 +728,7 @@ def bench_schedule_workload(args):
                 break
             n = int(min(tr.R, max(2 * n, n * (args.cpu_seconds / 2) / max(dt, 1e-3))))
         line["cpu_baseline"] = {"value": round(n / dt, 1), "unit": "queries/s (scheduler)",
-                                "cores": 1, "kind": "oracle",
+                                "cores": 1, "kind": "oracle", "cpu": cpu_model(),
                                 "sample": f"the oracle's choice over the first {n} queries of "
                                           f"the stream (hotness-aware policy), {dt:.1f} s"}
     print(json.dumps(line), flush=True)
@@ -688,7 +755,7 @@ def _prefix_cpu_baseline(workload, rng, H, D, scale, span, target_s):
             n = int(max(2 * n, n * (target_s / 2) / max(dt, 1e-3)))
         fl = 4.0 * len(rows) * span * D
         return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-                "kind": "oracle",
+                "kind": "oracle", "cpu": cpu_model(),
                 "sample": f"{len(rows)} random (prefix row, head) pairs of one {span}-token prefix, "
                           f"float64, {dt:.1f} s"}
     n_items = 1024
@@ -702,7 +769,7 @@ def _prefix_cpu_baseline(workload, rng, H, D, scale, span, target_s):
         n_items = int(min(20000, max(2 * n_items, n_items * (target_s / 2) / max(dt, 1e-3))))
     by = 4.0 * n_items * span * H * D * 2 + 4.0 * n_items * span * H
     return {"value": round(by / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n_items} items x {span} tokens, all heads, float64, {dt:.1f} s"}
 
 

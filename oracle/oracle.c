@@ -8,9 +8,10 @@
  * What it computes is the plain definition of the attention the Bat page
  * ("Bat: Efficient Generative Recommender Serving with Bipartite Attention")
  * describes for generative-recommender prefill:
- *   - user and item tokens are order-agnostic (section "This paper's idea",
- *     and "Why it works": permutation invariance), so there is no positional
- *     encoding and no causal mask;
+ *   - neither the history nor the items carry positions, and the two
+ *     groups can trade places (section "This paper's idea", and "Why it
+ *     works": permutation invariance), so there is no positional encoding
+ *     and no causal mask;
  *   - one group (the prefix: a user's history, or a set of cached items)
  *     has its key/value cache built once and reused (section "Problem",
  *     "Why this problem is worth solving"); reusing it is only exact if the

@@ -391,6 +391,48 @@ def attn_prefill(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
     return out, lse
 
 
+class PreparedPrefill:
+    """One bat_attn_prefill call with its arguments marshalled once: calling
+    it enqueues the call on the current stream (no per-call tensor checks or
+    workspace sizing).  The tensors must stay alive and unchanged in shape."""
+
+    def __init__(self, q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
+                 user_pool, item_pool, softmax_scale, max_suffix_len, max_prefix_len, out, lse,
+                 workspace):
+        torch = _torch()
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+            _need(t, n, q.dtype)
+        _need(cu_suffix_lens, "cu_suffix_lens", torch.int32)
+        _need(prefix_lens, "prefix_lens", torch.int32)
+        _need(prefix_mode, "prefix_mode", torch.uint8)
+        if block_table is not None:
+            _need(block_table, "block_table", torch.int32)
+        if lse is not None:
+            _need(lse, "lse", torch.float32)
+        total, H, D = q.shape
+        B = cu_suffix_lens.shape[0] - 1
+        dt = _dtype_code(q)
+        need = workspace_size(B, H, D, dt, total, max_suffix_len, max_prefix_len)
+        if workspace.numel() < need:
+            raise BatError(BAT_ERR_WORKSPACE, "PreparedPrefill")
+        self._keep = (q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table, out, lse,
+                      workspace)
+        self._up = user_pool.struct() if user_pool is not None else None
+        self._ip = item_pool.struct() if item_pool is not None else None
+        self._args = (
+            _ptr(q), _ptr(k), _ptr(v), _ptr(cu_suffix_lens), _ptr(prefix_lens),
+            _ptr(prefix_mode), _ptr(block_table),
+            0 if block_table is None else block_table.shape[1],
+            ctypes.byref(self._up) if self._up is not None else None,
+            ctypes.byref(self._ip) if self._ip is not None else None,
+            B, H, D, dt, float(softmax_scale), total, int(max_suffix_len), int(max_prefix_len),
+            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel())
+        self._fn = load().bat_attn_prefill
+
+    def __call__(self):
+        _check(self._fn(*self._args, _stream()), "bat_attn_prefill")
+
+
 def attn_prefill_noalloc(q, k, v, cu_suffix_lens, prefix_lens, prefix_mode, block_table,
                          user_pool, item_pool, softmax_scale, max_suffix_len, max_prefix_len,
                          out, lse=None):

@@ -122,6 +122,14 @@ class DeviceWorkload:
                                self.wl.total_s, self.max_s, self.max_p)
         return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
 
+    def prepared(self, out, lse, workspace):
+        """bat_attn_prefill over this workload with its arguments marshalled
+        once (api.PreparedPrefill)."""
+        return api.PreparedPrefill(self.q, self.k, self.v, self.cu_s, self.prefix_lens,
+                                   self.prefix_mode, self.block_table, self.user_pool,
+                                   self.item_pool, self.wl.scale, self.max_s, self.max_p, out,
+                                   lse, workspace)
+
     def run(self, out=None, lse=None, workspace=None, want_lse=True, block_table=None):
         return api.attn_prefill(self.q, self.k, self.v, self.cu_s, self.prefix_lens,
                                 self.prefix_mode,

@@ -175,3 +175,24 @@ def test_cached_equals_recompute_ping_pong(gpu_ready):
         rows_r = np.arange(f1 - (s1 - s0), f1)
         check_close(got_c[s0:s1], got_r[rows_r], "bf16", strict_abs=4e-3)
         assert np.abs(lc[:, s0:s1] - lrc[:, rows_r]).max() < 1e-3
+
+
+def test_prepared_call_matches_the_plain_call(gpu_ready):
+    """api.PreparedPrefill (arguments marshalled once, as the benchmark calls
+    the library) enqueues the same call: bitwise the same rows, call after
+    call."""
+    import torch
+    from prefix_reuse_attention_amd.device import DeviceWorkload
+    wl = W.make_custom(dtype="bf16", H=2, D=64, n_s=[256] * 4, n_p=[1024, 64, 0, 777],
+                       mode=[W.USER] * 4, seed=220, name="prepared")
+    print("[bitwise] prepared call", flush=True)
+    dw = DeviceWorkload(wl)
+    o1, l1 = dw.run(want_lse=True)
+    out, lse = torch.empty_like(o1), torch.empty_like(l1)
+    call = dw.prepared(out, lse, dw.workspace())
+    for _ in range(3):
+        out.zero_()
+        call()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_host(out), _host(o1))
+        np.testing.assert_array_equal(lse.cpu().numpy(), l1.cpu().numpy())

@@ -66,7 +66,8 @@ def bf16_kernel_label(wl):
     (256 rows per item) when suffixes average at least 192 rows (and, at
     D=64, the longest prefix has at least 4096 keys), else four;
     with eight waves and head dim 128 the ping-pong kernel.  Buffer-load
-    gathers (pools under 2 GiB)."""
+    copies (the global-load form only serves per-key pools of 2 GiB or
+    more)."""
     waves = 8 if wl.total_s >= 192 * wl.B and (wl.D == 128 or int(wl.n_p.max()) >= 4096) else 4
     if waves == 8 and wl.D == 128:
         return "attn_bf16_pp_kernel<128, false>"

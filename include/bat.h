@@ -63,8 +63,9 @@
  *                            and, at D=64, the longest prefix has >= 4096
  *                            keys; else 4)
  *       BAT_GATHER=flat      per-key gathers of small pool blocks by global
- *                            loads (the form pools of 2 GiB or more take)
- *                            instead of buffer loads
+ *                            loads (the form a pool of blocks smaller than
+ *                            a key tile takes at 2 GiB or more) instead of
+ *                            buffer loads
  *       BAT_SPLIT_CHUNK=n    split every prefix into chunks of n keys
  *                            (rounded up to the key tile) merged by
  *                            log-sum-exp; a value above every prefix never

@@ -1329,10 +1329,17 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
                             hipStream_t stream) {
   clear_stale_launch_error();
   if (grid <= 0) return hipSuccess;
+  // Only per-key gathers (pool blocks smaller than a key tile) address the
+  // whole pool from one descriptor with 32-bit offsets; whole-block tiles
+  // take a 64-bit base per tile, so a pool of any size copies them by buffer
+  // loads.  The global-load gather form is needed only for a per-key pool of
+  // 2 GiB or more.
   bool flat = flat_gather;
+  const int bn = D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN;
   for (int m = 0; m < 2; ++m)
-    flat |= (int64_t)p.pool_blocks[m] * p.H_kv * ((int64_t)2 * D << p.pool_bs_log2[m]) >
-            kBufferPoolLimit;
+    flat |= (1 << p.pool_bs_log2[m]) < bn &&
+            (int64_t)p.pool_blocks[m] * p.H_kv * ((int64_t)2 * D << p.pool_bs_log2[m]) >
+                kBufferPoolLimit;
   if (p.fp8 && D == 128 && W != 4) return hipErrorInvalidValue;  // fp8: four waves at D=128
   if (D == 128 && W == 8)
     launch_pp<128>(p, flat, grid, stream);

@@ -72,6 +72,20 @@ def test_bf16_small_blocks(gpu_ready, monkeypatch, D, gather):
         _compare_full(wl)
 
 
+@pytest.mark.slow
+def test_bf16_user_pool_beyond_2gib(gpu_ready):
+    """A user pool of 2.3 GB per tensor (70000 blocks of 64 tokens, H=2,
+    D=128), the requests' blocks scattered over all of it: whole-block tiles
+    take a 64-bit base per tile, so the buffer-load copy form serves a pool of
+    any size (only per-key gathers need the global-load form past 2 GiB)."""
+    wl = W.make_custom(dtype="bf16", H=2, D=128, n_s=[256, 200], n_p=[4096, 1000],
+                       mode=[W.USER, W.USER], seed=56, extra_user_blocks=70000,
+                       name="bf16_pool_2gib")
+    assert wl.user_num_blocks * wl.H * 64 * wl.D * 2 > 2 ** 31
+    assert wl.block_table.max() > 65536
+    _compare_full(wl)
+
+
 def test_bf16_empty_requests_and_suffix_only(gpu_ready):
     """Requests with no suffix rows write nothing; n_p = 0 is pure suffix
     self-attention (the empty prefix partial merges as the identity)."""

@@ -285,6 +285,7 @@ def main():
         "suffix_tokens_per_s": round(tok_s, 1),
         "alg_flops_per_step": flops,
         "alg_bytes_per_step": alg_bytes,
+        "prefix_unique": unique_prefix(wl),
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
@@ -364,6 +365,27 @@ def bench_fp8_workload(args):
                          "kernel": f"attn_bf16_kernel<{wl.D}, 4, false, true>",
                          "kernel_ms_mean": round(kernel_ms, 5)}}
     print(json.dumps(line), flush=True)
+
+
+def unique_prefix(wl):
+    """The distinct prefix blocks a batch reads, beside the algorithmic bytes
+    (which count every request's prefix once): item blocks listed by several
+    requests, and user pages, each counted once.  The gap between the two is
+    the reuse an item-as-prefix batch gets from the pool."""
+    from prefix_reuse_attention_amd import workloads as W
+    e = 2 if wl.dtype == "bf16" else 4
+    items, user_tokens, listed = set(), 0, 0
+    for r in range(wl.B):
+        n = int(wl.n_p[r])
+        if wl.mode[r] == W.ITEM:
+            ids = wl.block_table[r, : n // W.ITEM_TOKENS]
+            items.update(int(i) for i in ids)
+            listed += len(ids)
+        else:
+            user_tokens += n
+    tokens = len(items) * W.ITEM_TOKENS + user_tokens
+    return {"item_blocks_listed": listed, "item_blocks_unique": len(items),
+            "kv_bytes_unique": tokens * wl.H * wl.D * e * 2}
 
 
 def run_cpu_baseline(wl, target_s):

@@ -608,9 +608,9 @@ __device__ __forceinline__ void copies_landed_barrier() {
 // block and head).  Each thread owns NP 16-byte pieces (16 codes of one key
 // row) of K and of V: during the compute of tile t it loads the pieces of
 // tile t+1 into registers with their blocks' scales (the block ids were
-// loaded during tile t-1), and after that compute it converts them --
-// code value * scale, exact in bfloat16 -- into the next LDS stage in the
-// stage's swizzled layout.  The kernel's compute is then the bfloat16 one.
+// loaded during tile t-1), and after that compute it converts them -- code
+// value * scale, exact in bfloat16 -- into the next LDS stage in the stage's
+// swizzled layout.  The kernel's compute is then the bfloat16 one.
 template <int D, int W>
 struct Fp8Prefix {
   using C = Bf16Cfg<D>;
@@ -618,23 +618,40 @@ struct Fp8Prefix {
   static constexpr int CPR8 = D / 16;         // 16-byte pieces of codes per key row
   static constexpr int NP = C::BN * CPR8 / THREADS;
   static_assert(NP >= 1 && NP * THREADS == C::BN * CPR8, "pieces per thread");
+  static_assert(D == 128 || D == 64, "the piece mapping below covers these head dims");
   const uint8_t *pk, *pv;                     // code pools
   const float *sk, *sv;                       // scales [blocks, H_kv]
   const int32_t *bt_row;
   int lg, blocks, bt_stride, H, head, p_begin, p_end;
-  int row[NP], c[NP];
+  int row[NP], c;
   int blk[NP];                                // block of each piece's row, next tile
   u32x4 dk[NP], dv[NP];
   float fk[NP], fv[NP];
   bool bad = false;
 
+  // Which piece a thread converts.  LDS takes a 64-lane 16-byte store eight
+  // lanes at a time, 128 bytes a cycle, so eight consecutive lanes have to
+  // store to eight different 16-byte slots of a 128-byte bank line.  Piece c
+  // of row r is stored as chunks 2c and 2c+1, at (2c) ^ swz(r) and
+  // (2c+1) ^ swz(r): four pieces of one row take four slots of one parity,
+  // that of bit 0 of the swizzle, (r >> 2) & 1.  So each eight lanes take
+  // four pieces of row r and the same four of row r+4 (D=128: lanes 0-3 and
+  // 8-11 of sixteen hold row r, 4-7 and 12-15 row r+4; D=64, a row being four
+  // pieces: rows b, b+4, b+1, b+5 in four-lane runs, so that sixteen lanes
+  // also cover a 256-byte line once).  Each run of four lanes reads 64
+  // contiguous bytes of codes.
   __device__ __forceinline__ void init(int tid) {
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int g = tid + THREADS * j;
-      row[j] = g / CPR8;
-      c[j] = g % CPR8;
+    const int k = tid >> 4, l = tid & 15;
+    int r0;
+    if constexpr (D == 128) {
+      r0 = (k & 3) + 8 * (k >> 2) + 4 * ((l >> 2) & 1);
+      c = 4 * (l >> 3) + (l & 3);
+    } else {
+      r0 = 2 * (k & 1) + 8 * (k >> 1) + ((0x5140 >> (4 * (l >> 2))) & 0xF);
+      c = l & 3;
     }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) row[j] = r0 + (THREADS / CPR8) * j;
   }
   __device__ __forceinline__ void load_ids(int tile) {
 #pragma unroll
@@ -654,7 +671,7 @@ struct Fp8Prefix {
       fk[j] = fv[j] = 0.f;
       if (key < p_end && inb) {
         const int64_t bh = (int64_t)blk[j] * H + head;
-        const int64_t off = ((bh << lg) | (key & ((1 << lg) - 1))) * D + c[j] * 16;
+        const int64_t off = ((bh << lg) | (key & ((1 << lg) - 1))) * D + c * 16;
         dk[j] = *(const u32x4 *)(pk + off);
         dv[j] = *(const u32x4 *)(pv + off);
         fk[j] = sk[bh];
@@ -677,8 +694,8 @@ struct Fp8Prefix {
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int sw = swz<D>(row[j]);
-      const int o0 = row[j] * C::RB + (((2 * c[j]) ^ sw) << 4);
-      const int o1 = row[j] * C::RB + (((2 * c[j] + 1) ^ sw) << 4);
+      const int o0 = row[j] * C::RB + (((2 * c) ^ sw) << 4);
+      const int o1 = row[j] * C::RB + (((2 * c + 1) ^ sw) << 4);
       u32x4 lo, hi;
       convert(dk[j], fk[j], lo, hi);
       *(u32x4 *)(kl + o0) = lo;

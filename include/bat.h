@@ -59,9 +59,11 @@
  *     every kernel form; none changes what is computed, only how):
  *       BAT_VALIDATE=1       the device checks above
  *       BAT_WAVES=4|8        bf16 rows per work item: 4 or 8 waves of 32 rows
- *                            (default: 8 when suffixes average >= 192 rows
- *                            and, at D=64, the longest prefix has >= 4096
- *                            keys; else 4)
+ *                            (default: 8 when suffixes average >= 192 rows,
+ *                            else 4; also 4 at D=64 when a bfloat16 pool's
+ *                            blocks hold fewer than 64 tokens, and for fp8
+ *                            pools at D=128).  Workspace sizes cover either
+ *                            shape.
  *       BAT_GATHER=flat      per-key gathers of small pool blocks by global
  *                            loads (the form a pool of blocks smaller than
  *                            a key tile takes at 2 GiB or more) instead of

@@ -35,7 +35,7 @@ hipError_t launch_item_local(const void *q, const void *k, const void *v, int32_
                              const int32_t *cu_s, const int32_t *prefix_lens, int32_t B,
                              int32_t max_prefix, hipStream_t stream);
 int bf16_rows_per_item(int W);
-int bf16_keys_per_tile(int D);
+int bf16_keys_per_tile(int D, int W, bool fp8);
 int f32_rows_per_item();
 int f32_keys_per_tile();
 
@@ -127,20 +127,23 @@ struct Fp8Scales {
 // prefix_only: the rows see their prefix only and every row gets an fp32
 // partial (candidate-isolated suffixes); prefixes are then never split.
 // hg: query heads per key/value head (grouped heads; 1 otherwise).
+// per_key: a prefix pool's blocks are smaller than the eight-wave kernel's
+// key tile, so its tiles are gathered key by key.
 bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
                int32_t max_p, Plan &pl, bool prefix_only = false, int32_t hg = 1,
-               bool allow_split = true, bool fp8 = false) {
+               bool allow_split = true, bool fp8 = false, bool per_key = false) {
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
-  // bf16: eight waves (256 rows) share each K/V tile when the suffixes are
-  // long enough to fill them, else four (128 rows).  At D=64 the shared tile
-  // only pays with long prefixes (measured: eight waves ahead from about
-  // 4096 prefix keys, four ahead below)
+  // bf16: eight waves (256 rows, the ping-pong kernel) share each K/V tile
+  // when the suffixes are long enough to fill them, else four (128 rows).
+  // At D=64 the ping-pong kernel's 64-key tiles pay when whole pool blocks
+  // are copied; per-key gathers run faster in the four-wave kernel's
+  // 128-key tiles (measured: config 2 +11 % on eight waves, config 3 -8 %).
   if (const char *e = std::getenv("BAT_WAVES")) {
     pl.waves = std::atoi(e) == 8 ? 8 : 4;
   } else {
-    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B && (D == 128 || max_p >= 4096))
-                   ? 8 : 4;
+    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B &&
+                !(D == 64 && per_key && !fp8)) ? 8 : 4;
   }
   // fp8 pools: the four-wave kernel at head dim 128 (the eight-wave one
   // copies every tile straight into LDS, with no place to convert codes)
@@ -149,7 +152,7 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   // the global-load form that pools of 2 GiB or more need
   if (const char *e = std::getenv("BAT_GATHER")) pl.flat_gather = std::strcmp(e, "flat") == 0;
   pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
-  pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D) : f32_keys_per_tile();
+  pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D, pl.waves, fp8) : f32_keys_per_tile();
   // Split a prefix only when the unsplit batch cannot fill the GPU
   // (about two items per CU on 256 CUs) and the prefix is long.
   const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
@@ -187,6 +190,23 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   pl.off_part_lse = off; off = align256(off + sizeof(float) * (size_t)pl.part_rows * H);
   pl.total = off;
   return true;
+}
+
+// The workspace a call needs whatever its pools hold: the larger of the
+// plans with and without per-key gathers (which may change the workgroup
+// shape).  Returns 0 if no plan exists.
+size_t plan_bound(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, int32_t max_s,
+                  int32_t max_p, bool prefix_only = false, int32_t hg = 1,
+                  bool allow_split = true, bool fp8 = false) {
+  size_t n = 0;
+  for (bool per_key : {false, true}) {
+    Plan pl;
+    if (!make_plan(B, H, D, dt, total_s, max_s, max_p, pl, prefix_only, hg, allow_split, fp8,
+                   per_key))
+      return 0;
+    if (pl.total > n) n = pl.total;
+  }
+  return n;
 }
 
 bat_status pool_desc(const bat_kv_pool *pool, const void *&k, const void *&v, int32_t &blocks,
@@ -268,9 +288,7 @@ bat_status bat_kv_build(const void *k, const void *v, const int32_t *cu_lens,
 size_t bat_attn_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
                                int32_t total_suffix, int32_t max_suffix_len,
                                int32_t max_prefix_len) {
-  Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl)) return 0;
-  return pl.total;
+  return plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len);
 }
 
 bat_status bat_kv_build_fp8(const void *k, const void *v, const int32_t *cu_lens,
@@ -328,9 +346,9 @@ size_t bat_attn_prefill_workspace_size(int32_t B, int32_t H, int32_t D, int32_t 
   size_t n = 0;
   for (bat_dtype dt : {BAT_F32, BAT_BF16}) {
     if (!supported(dt, D)) continue;
-    Plan pl;
-    if (!make_plan(B, H, D, dt, total_suffix, total_suffix, max_prefix_len, pl)) return 0;
-    if (pl.total > n) n = pl.total;
+    const size_t t = plan_bound(B, H, D, dt, total_suffix, total_suffix, max_prefix_len);
+    if (t == 0) return 0;
+    if (t > n) n = t;
   }
   return n;
 }
@@ -363,12 +381,22 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
   if (max_prefix_len > 0 && p.pool_blocks[0] == 0 && p.pool_blocks[1] == 0)
     return BAT_ERR_INVALID_ARG;
   const int32_t hg = H_kv > 0 ? H / H_kv : 1;
+  // a pool whose blocks are smaller than the eight-wave kernel's key tile
+  // is gathered key by key
+  const int pp_keys = bf16_keys_per_tile(D, 8, false);
+  bool per_key = false;
+  for (int i = 0; i < 2; ++i)
+    per_key |= p.pool_blocks[i] > 0 && (1 << p.pool_bs_log2[i]) < pp_keys;
   Plan pl;
   if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, prefix_only, hg,
-                 allow_split, f8 != nullptr))
+                 allow_split, f8 != nullptr, per_key))
     return BAT_ERR_INVALID_ARG;
   if (!workspace) return BAT_ERR_WORKSPACE;
-  if (workspace_bytes < pl.total) return BAT_ERR_WORKSPACE;
+  // the call asks for what its size function reports (the bound over both
+  // gather forms), not only what this plan uses
+  if (workspace_bytes < plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len,
+                                   prefix_only, hg, allow_split, f8 != nullptr))
+    return BAT_ERR_WORKSPACE;
 
   uint8_t *ws = (uint8_t *)workspace;
   if (f8) {
@@ -570,16 +598,13 @@ bat_status bat_attn_prefill_noalloc(const void *q, const void *k, const void *v,
   // the plan bat_attn_prefill would take; when its split partials do not
   // fit the scratch, the same call unsplit (the rows are the same up to
   // rounding); beyond that, the batch is too large for this entry point
-  Plan pl;
   bool allow_split = true;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl))
-    return BAT_ERR_INVALID_ARG;
-  if (pl.total > kNoAllocScratchBytes) {
+  size_t need = plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len);
+  if (need == 0) return BAT_ERR_INVALID_ARG;
+  if (need > kNoAllocScratchBytes) {
     allow_split = false;
-    if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, false, 1,
-                   false) ||
-        pl.total > kNoAllocScratchBytes)
-      return BAT_ERR_WORKSPACE;
+    need = plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, false, 1, false);
+    if (need == 0 || need > kNoAllocScratchBytes) return BAT_ERR_WORKSPACE;
   }
   void *ws = nullptr;
   const bat_status s = scratch_of_current_device(&ws);
@@ -633,10 +658,7 @@ size_t bat_attn_gqa_workspace_size(int32_t B, int32_t H, int32_t H_kv, int32_t D
                                    int32_t total_suffix, int32_t max_suffix_len,
                                    int32_t max_prefix_len) {
   if (H_kv <= 0 || H % H_kv != 0) return 0;
-  Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, false, H / H_kv))
-    return 0;
-  return pl.total;
+  return plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, false, H / H_kv);
 }
 
 bat_status bat_attn_prefill_gqa(const void *q, const void *k, const void *v,
@@ -667,9 +689,7 @@ bat_status bat_attn_prefill_gqa(const void *q, const void *k, const void *v,
 size_t bat_attn_isolated_workspace_size(int32_t B, int32_t H, int32_t D, bat_dtype dt,
                                         int32_t total_suffix, int32_t max_suffix_len,
                                         int32_t max_prefix_len) {
-  Plan pl;
-  if (!make_plan(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, pl, true)) return 0;
-  return pl.total;
+  return plan_bound(B, H, D, dt, total_suffix, max_suffix_len, max_prefix_len, true);
 }
 
 bat_status bat_attn_prefill_isolated(const void *q, const void *k, const void *v,

@@ -49,29 +49,33 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
 constexpr int64_t kBufferPoolLimit = 0x7FFFFFF0;
 constexpr int kPastPool = 0x7FFFFFF0;
 
-// Workgroup shape: W waves of 32 query rows share every K/V tile; each wave
-// copies 16/W of the tile's 16 one-kilobyte pieces of K and of V.
+// Workgroup shape: W waves of 32 query rows share every K/V tile.
 template <int W>
 struct WgCfg {
   static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * W;
   static constexpr int ROWS = 32;                   // query rows per wave
   static constexpr int BM = W * ROWS;               // query rows per item
-  static constexpr int CPW = 16 / W;                // copy instructions per wave per tile
 };
 
-// Tile geometry (depends on the head dim only).
-template <int D>
+// Keys per tile of the four-wave kernel: a 16 KB tile of K (and of V) at
+// either head dim.  The ping-pong kernel takes 64-key tiles at both.
+constexpr int bf16_default_bn(int D) { return D == 128 ? 64 : 128; }
+constexpr int kPpBN = 64;
+
+// Tile geometry: head dim and keys per tile.
+template <int D, int BN_ = bf16_default_bn(D)>
 struct Bf16Cfg {
-  static constexpr int BN = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int BN = BN_;                    // keys per tile
   static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   static constexpr int RB = D * 2;                  // bytes per K/V row
   static constexpr int RPI = 64 / CPR;              // rows per wave copy instruction
   static constexpr int TILE = BN * RB;              // bytes of one K (or V) tile
+  static constexpr int PIECES = TILE / 1024;        // one-kilobyte copy pieces per tile
   static constexpr int NB = BN / 32;                // 32-key MFMA blocks per tile
   static constexpr int ND = D / 32;                 // 32-wide d blocks of O
   static constexpr int KK = D / 16;                 // k-steps of QK^T
-  static_assert(TILE == 16384, "16 one-kilobyte copy pieces per tile");
+  static_assert(TILE % 1024 == 0 && BN % 32 == 0, "whole pieces, whole MFMA blocks");
 };
 
 // Chunk swizzle of K/V row r: chunk c of the row is stored at c ^ swz(r).
@@ -229,10 +233,13 @@ struct LdsOffsets {
 // on the LDS counter too, so while one can be in flight every LDS read has
 // to be waited for in full.  A block id out of range is remembered in
 // `bad` and reported once, after the loop.
-template <int D, int W, bool FLAT>
+template <int D, int W, bool FLAT, int BN_ = bf16_default_bn(D)>
 struct TileCopy {
-  using C = Bf16Cfg<D>;
-  static constexpr int CPW = WgCfg<W>::CPW;
+  using C = Bf16Cfg<D, BN_>;
+  // copy instructions per wave per tile: each of the W copying waves takes
+  // PIECES / W of the tile's one-kilobyte pieces of K and of V
+  static constexpr int CPW = C::PIECES / W;
+  static_assert(CPW >= 1 && CPW * W == C::PIECES, "pieces per copying wave");
   const uint8_t *pool_k, *pool_v, *ks, *vs;  // prefix pool / suffix K,V bases
   const int32_t *bt_row;                     // this request's block-table row
   int lg, blocks, bt_stride, H, head, q0, n_s, p_begin, p_end, n_tiles_p, n_tiles;
@@ -802,7 +809,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   // Every copy writes its whole stage (lanes past the end of the data write
   // zeros), so the stages need no clearing.  The Q loads go out between the
   // block-id load of tile 0 and its copy, so that the latencies overlap.
-  int ids[G::CPW];  // (fp8 pools: never read, suffix tiles plan without them)
+  int ids[TileCopy<D, W, FLAT>::CPW];  // (fp8 pools: never read, suffix tiles plan without them)
   // fp8 pool: the prefix tiles come through f8 (register-staged, converted
   // to bfloat16 into the stage); suffix tiles are copied as usual
   Fp8Prefix<D, W> f8;
@@ -846,7 +853,7 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   // Tile t is consumed from one stage while the copy of tile t+1 into the
   // other goes out one instruction every SPACING S^T MFMAs (a tile past the
   // last copies nothing).
-  constexpr int SPACING = (C::NB * C::KK) / (2 * G::CPW);
+  constexpr int SPACING = (C::NB * C::KK) / (2 * TileCopy<D, W, FLAT>::CPW);
   auto tile_step = [&](int t, uint8_t *kc, uint8_t *vc, uint8_t *kn, uint8_t *vn)
       __attribute__((always_inline)) {
     if (FP8 && t + 1 < cp.n_tiles_p) {
@@ -933,12 +940,14 @@ __device__ __forceinline__ void static_for(F &&f) {
 // K(t) and V(t) sit in stage t % 2.  The copy of K(t+1) replaces K(t-1) and
 // that of V(t) replaces V(t-2), both last read in step t-1; they land before
 // the barrier that ends step t.  Group B issues every copy, spread over its
-// softmax.  For head dim 64 (128-key tiles, twice the exponentials per MFMA)
-// the softmax outweighs the MFMAs and the kernel above serves instead.
+// softmax.  Tiles are 64 keys at both head dims: at D=64 a 64-key tile
+// keeps the score, probability and output registers of a wave small enough
+// for two waves per SIMD, and its softmax phase (twice the exponentials per
+// MFMA of D=128) still runs under the other group's MFMAs for most of it.
 template <int D, bool FLAT>
 __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
-  using C = Bf16Cfg<D>;
-  using TC = TileCopy<D, 4, FLAT>;  // group B's four waves copy every tile
+  using C = Bf16Cfg<D, kPpBN>;
+  using TC = TileCopy<D, 4, FLAT, kPpBN>;  // group B's four waves copy every tile
   constexpr int CPW = TC::CPW;
   constexpr int NS = C::NB * C::KK;
   constexpr int NV = 2 * C::ND;
@@ -1315,11 +1324,16 @@ template __global__ void attn_bf16_kernel<64, 4, false, true>(AttnParams);
 template __global__ void attn_bf16_kernel<64, 8, false, true>(AttnParams);
 template __global__ void attn_bf16_pp_kernel<128, false>(AttnParams);
 template __global__ void attn_bf16_pp_kernel<128, true>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 8, false, false>(AttnParams);
-template __global__ void attn_bf16_kernel<64, 8, true, false>(AttnParams);
+template __global__ void attn_bf16_pp_kernel<64, false>(AttnParams);
+template __global__ void attn_bf16_pp_kernel<64, true>(AttnParams);
 
 int bf16_rows_per_item(int W) { return W == 8 ? WgCfg<8>::BM : WgCfg<4>::BM; }
-int bf16_keys_per_tile(int D) { return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN; }
+// keys per tile of the kernel a plan launches: the ping-pong kernel for
+// eight waves (fp8 pools excepted), else the four-wave (or fp8) kernel
+int bf16_keys_per_tile(int D, int W, bool fp8) {
+  if (W == 8 && !fp8) return kPpBN;
+  return D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN;
+}
 
 template <int D, int W>
 static void launch_one(const AttnParams &p, bool flat, int grid, hipStream_t stream) {
@@ -1352,7 +1366,7 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
   // loads.  The global-load gather form is needed only for a per-key pool of
   // 2 GiB or more.
   bool flat = flat_gather;
-  const int bn = D == 128 ? Bf16Cfg<128>::BN : Bf16Cfg<64>::BN;
+  const int bn = bf16_keys_per_tile(D, W, p.fp8 != 0);
   for (int m = 0; m < 2; ++m)
     flat |= (1 << p.pool_bs_log2[m]) < bn &&
             (int64_t)p.pool_blocks[m] * p.H_kv * ((int64_t)2 * D << p.pool_bs_log2[m]) >
@@ -1362,8 +1376,11 @@ hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather,
     launch_pp<128>(p, flat, grid, stream);
   else if (D == 128 && W == 4)
     launch_one<128, 4>(p, flat, grid, stream);
+  else if (D == 64 && W == 8 && p.fp8)  // fp8 pools: the eight-wave kernel with the fp8 path
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 8, false, true>), dim3(grid), dim3(512), 0, stream,
+                       p);
   else if (D == 64 && W == 8)
-    launch_one<64, 8>(p, flat, grid, stream);
+    launch_pp<64>(p, flat, grid, stream);
   else if (D == 64 && W == 4)
     launch_one<64, 4>(p, flat, grid, stream);
   else

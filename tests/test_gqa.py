@@ -5,7 +5,7 @@ H query heads share H_kv key/value heads; the pools are built with H_kv heads
 by bat_kv_build and the fresh suffix keys/values carry H_kv heads.  Cases:
 groups of 2, 4 and 8 query heads per key/value head, user and item prefixes,
 empty prefixes, both bf16 head dims and fp32, the four- and eight-wave
-kernels (the ping-pong one for D=128).  Every expected value comes from the
+kernels (the eight-wave one is the ping-pong kernel).  Every expected value comes from the
 oracle.
 """
 import numpy as np

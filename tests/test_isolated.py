@@ -4,7 +4,7 @@ against the oracle, through the C ABI.
 Each suffix row sees its request's prefix and the T tokens of its own
 candidate.  Cases: every supported T, both bf16 head dims and fp32, user and
 item prefixes in one batch, empty prefixes and empty suffixes, the four- and
-eight-wave kernels (the ping-pong one for D=128), the batch of single-token
+eight-wave kernels (the ping-pong kernel), the batch of single-token
 candidates of the 1024-history configuration on sampled rows, and
 single-token candidates on the ping-pong kernel, which folds each row's own
 key into its prefix result in one launch (ragged rows, a request with no
@@ -65,8 +65,8 @@ def test_isolated_fp32(gpu_ready, D):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_isolated_eight_wave_items(gpu_ready, D):
-    """Long suffixes: 256-row items (eight waves; the ping-pong kernel for
-    D=128) writing prefix partials, a ragged last row tile."""
+    """Long suffixes: 256-row items (eight waves, the ping-pong kernel)
+    writing prefix partials, a ragged last row tile."""
     wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=[512, 264], n_p=[700, 1031],
                        mode=[W.USER, W.USER], seed=120 + D, name=f"iso_w8_D{D}")
     _compare(wl, 4)

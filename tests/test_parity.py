@@ -58,13 +58,16 @@ def test_bf16_ragged_mixed(gpu_ready, D):
     _compare_full(wl)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("gather", ["buffer", "flat"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_bf16_small_blocks(gpu_ready, monkeypatch, D, gather):
+def test_bf16_small_blocks(gpu_ready, monkeypatch, D, gather, waves):
     """User pools with 1-, 2- and 16-token pages (the per-key gather path),
     in both gather forms: buffer loads with 32-bit offsets into the pool and
-    the global loads that pools of 2 GiB or more take."""
+    the global loads that pools of 2 GiB or more take; four-wave items and
+    the eight-wave (ping-pong) kernel."""
     monkeypatch.setenv("BAT_GATHER", gather)
+    monkeypatch.setenv("BAT_WAVES", waves)
     for bs in (1, 2, 16):
         wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=[40, 3], n_p=[77, 130],
                            mode=[W.USER, W.USER], seed=40 + bs, user_block_size=bs,
@@ -117,11 +120,13 @@ def test_bf16_increasing_scores(gpu_ready):
     _compare_full(wl)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
-def test_split_prefix_merge(gpu_ready, monkeypatch, dtype, D):
+@pytest.mark.parametrize("dtype,D,waves", [("bf16", 128, "4"), ("bf16", 64, "4"), ("f32", 64, "4"),
+                                           ("bf16", 128, "8"), ("bf16", 64, "8")])
+def test_split_prefix_merge(gpu_ready, monkeypatch, dtype, D, waves):
     """Prefixes split across workgroups (forced chunk length), recombined by
-    the log-sum-exp merge kernel."""
+    the log-sum-exp merge kernel; both bf16 workgroup shapes."""
     monkeypatch.setenv("BAT_SPLIT_CHUNK", "256")
+    monkeypatch.setenv("BAT_WAVES", waves)
     wl = W.make_custom(dtype=dtype, H=2, D=D, n_s=[90, 300, 1], n_p=[1000, 256, 2100],
                        mode=[W.USER, W.ITEM, W.USER], seed=80 + D, num_items=100,
                        name=f"split_{dtype}_D{D}")
@@ -143,12 +148,12 @@ def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
 @pytest.mark.parametrize("D", [64, 128])
 def test_bf16_tile_counts(gpu_ready, monkeypatch, D):
     """Items of 1 to 6 key tiles with eight waves per workgroup (the
-    head-dim-128 kernel alternates two wave groups over a two-phase step, with
-    a prologue tile and a last-tile tail): every count of steps around the
-    loop's unrolling, full and partial last tiles, prefix-only and
-    suffix-only tiles."""
+    ping-pong kernel alternates two wave groups over a two-phase step, with
+    a prologue tile and a last-tile tail; 64-key tiles at both head dims):
+    every count of steps around the loop's unrolling, full and partial last
+    tiles, prefix-only and suffix-only tiles."""
     monkeypatch.setenv("BAT_WAVES", "8")
-    bn = 64 if D == 128 else 128
+    bn = 64
     n_s = [bn, bn - 7, 2 * bn, 3, bn + 1, 2 * bn - 1]
     n_p = [0, bn, 2 * bn - 5, 2 * bn, 3 * bn + 9, 3 * bn]
     wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s, n_p=n_p, mode=[W.USER] * 6,

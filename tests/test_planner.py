@@ -46,9 +46,8 @@ def _check(wl, hdr, raw, H=None, hg=1):
     """H query heads (wl.H by default), hg of them per key/value head."""
     B, H = wl.B, (wl.H if H is None else H)
     total_s = int(wl.n_s.sum())
-    # eight-wave (256-row) items when suffixes average 192 rows or more and,
-    # at head dim 64, the longest prefix has at least 4096 keys
-    eight = total_s >= 192 * B and (wl.D == 128 or int(wl.n_p.max()) >= 4096)
+    # eight-wave (256-row) items when suffixes average 192 rows or more
+    eight = total_s >= 192 * B
     bm = 256 if eight else 128
     max_s = int(wl.n_s.max())
     t_max = -(-max_s // bm)

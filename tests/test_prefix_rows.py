@@ -61,8 +61,8 @@ def test_prefix_rows_ragged(gpu_ready, dtype, D):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_prefix_rows_eight_wave_items(gpu_ready, D):
-    """Long prefixes: 256-row items of the eight-wave kernels (the ping-pong
-    one for D=128), several row tiles per request and a ragged last tile."""
+    """Long prefixes: 256-row items of the eight-wave (ping-pong) kernel,
+    several row tiles per request and a ragged last tile."""
     lens = [700, 512, 1031]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     H = 2

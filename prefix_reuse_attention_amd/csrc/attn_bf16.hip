@@ -783,14 +783,10 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
   cp.n_tiles = n_tiles;
   __shared__ u32x4 s_tab[TileCopy<D, W, FLAT>::kTabTiles];
   cp.tab = s_tab;
-  cp.use_tab = n_tiles <= TileCopy<D, W, FLAT>::kTabTiles;
+  const bool use_tab = n_tiles <= TileCopy<D, W, FLAT>::kTabTiles;
+  cp.use_tab = false;  // tile 0 is planned from the block table (below)
   cp.dv_p = cp.pool_v - cp.pool_k;
   cp.dv_s = cp.vs - cp.ks;
-  if (cp.use_tab) {
-    cp.fill_tab(tid, G::THREADS);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
-    __syncthreads();                     // every entry visible
-  }
   LdsOffsets<D> lo;
   lo.init(lane);
 
@@ -808,7 +804,9 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
 
   // Every copy writes its whole stage (lanes past the end of the data write
   // zeros), so the stages need no clearing.  The Q loads go out between the
-  // block-id load of tile 0 and its copy, so that the latencies overlap.
+  // block-id load of tile 0 and its copy, so that the latencies overlap, and
+  // tile 0 is planned from the block table itself, so that its copy is in
+  // flight while the copy table is filled.
   int ids[TileCopy<D, W, FLAT>::CPW];  // (fp8 pools: never read, suffix tiles plan without them)
   // fp8 pool: the prefix tiles come through f8 (register-staged, converted
   // to bfloat16 into the stage); suffix tiles are copied as usual
@@ -846,9 +844,14 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnParams p) {
     f8.store(st0k, st0v);
   } else {
     cp.issue(0, ids, st0k, st0v);
-    if constexpr (!FP8) cp.load_ids(1, ids);
   }
-  copies_landed_barrier();  // tile 0 in LDS, Q in registers
+  cp.use_tab = use_tab;
+  if constexpr (!FP8) cp.load_ids(1, ids);
+  if (use_tab) {
+    cp.fill_tab(tid, G::THREADS);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
+  }
+  copies_landed_barrier();  // tile 0 in LDS, Q in registers, every table entry visible
 
   // Tile t is consumed from one stage while the copy of tile t+1 into the
   // other goes out one instruction every SPACING S^T MFMAs (a tile past the
@@ -1020,11 +1023,6 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   cp.use_tab = n_tiles <= TC::kTabTiles;
   cp.dv_p = cp.pool_v - cp.pool_k;
   cp.dv_s = cp.vs - cp.ks;
-  if (cp.use_tab) {
-    cp.fill_tab(tid, 512);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
-    __syncthreads();                     // every entry visible
-  }
   LdsOffsets<D> lo;
   lo.init(lane);
 
@@ -1091,8 +1089,10 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   // running max m_run with no row maximum on the common path: a 32-key
   // block is kept when no lane's share of its row sum exceeds 2^8, which
   // bounds every probability by 2^8 (the lazy-rescale bound).  Otherwise
-  // (always on an item's first tile, rarely later) the tile's row maximum
-  // is taken, O and l are rescaled and the tile's probabilities recomputed.
+  // (rarely after an item's first tile) the tile's row maximum is taken, O
+  // and l are rescaled and the tile's probabilities recomputed.  An item's
+  // first tile, where the running max is not yet a row value, takes the row
+  // maximum first and computes its probabilities once.
   // hook(k) runs after pair k (group B issues its copies there).
   auto softmax = [&](int t, auto &&hook) __attribute__((always_inline)) {
     const int valid = valid_keys(t);
@@ -1123,16 +1123,21 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
         bl[nb] = sa + sb;
       }
     };
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float mloc = max16(s[0]);
+#pragma unroll
+      for (int nb = 1; nb < C::NB; ++nb) mloc = fmaxf(mloc, max16(s[nb]));
+      return row_max_both_halves(mloc) * cs;
+    };
+    // first tile: o and the row sum are still zero, so only the running max
+    // moves; every probability is then at most 1 and the check below passes
+    if (t == 0) m_run = fmaxf(m_run, tile_max());
     probs(-m_run, true);
     bool over = false;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) over |= !(bl[nb] <= kTauSum);
     if (__any(over)) {
-      float mloc = max16(s[0]);
-#pragma unroll
-      for (int nb = 1; nb < C::NB; ++nb) mloc = fmaxf(mloc, max16(s[nb]));
-      const float mt = row_max_both_halves(mloc) * cs;
-      const float m_new = fmaxf(m_run, mt);
+      const float m_new = fmaxf(m_run, tile_max());
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       la *= alpha;
 #pragma unroll
@@ -1152,7 +1157,10 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: Q, the copy of K(0) (group B), barrier
+  // ---- prologue: Q, the copy of K(0) (group B), the copy table, barrier.
+  // K(0) is planned from the block table itself, so that its copy is in
+  // flight while the table is filled: one memory round trip before the
+  // first tile instead of two.
   int ids[CPW];
   typename TC::Plan pl_v;  // the plan of the tile whose V goes out next
   {
@@ -1165,13 +1173,20 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
     }
   }
   if (!grp_a) {
+    const bool tab = cp.use_tab;
+    cp.use_tab = false;
     cp.load_ids(0, ids);
     pl_v = cp.plan(0, ids);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) cp.fire(pl_v, j, k0, v0);
+    cp.use_tab = tab;
     cp.load_ids(1, ids);
   }
-  copies_landed_barrier();
+  if (cp.use_tab) {
+    cp.fill_tab(tid, 512);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's entries stored
+  }
+  copies_landed_barrier();  // K(0) and Q landed, every table entry visible
 
   auto pv_only = [&](const uint8_t *vl) __attribute__((always_inline)) {
     bf16x8 r[3];

@@ -976,6 +976,12 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   const bool grp_a = wave < 4;
 
   const int row = it.m_tile * BM + wave * 32 + col;
+  // A wave whose 32 rows all lie past the suffix's end (the last row tile
+  // of a suffix that is not a multiple of 256 rows) computes nothing: it
+  // skips its operand reads, MFMAs and softmax, and keeps only its part in
+  // the barriers and, in group B, in the copies.
+  const bool live =
+      __builtin_amdgcn_readfirstlane((int)(it.m_tile * BM + wave * 32 < x.n_s)) != 0;
   const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
   bf16x8 qf[C::KK];
 
@@ -1060,6 +1066,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   // The MFMA phase: O += V(t-1)^T P(t-1)^T (when PV), then S(t)^T, operand
   // reads two MFMAs ahead through three rotating registers.
   auto gemm = [&](const uint8_t *kt, const uint8_t *vp, auto pv_c) __attribute__((always_inline)) {
+    if (!live) return;
     constexpr bool PV = decltype(pv_c)::value;
     constexpr int N0 = PV ? NPV : 0, N = N0 + NS;
     auto op = [&](int j) __attribute__((always_inline)) {
@@ -1095,6 +1102,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   // maximum first and computes its probabilities once.
   // hook(k) runs after pair k (group B issues its copies there).
   auto softmax = [&](int t, auto &&hook) __attribute__((always_inline)) {
+    if (!live) {  // only the copies the hook issues
+#pragma unroll
+      for (int k = 0; k < 8 * C::NB; ++k) hook(k);
+      return;
+    }
     const int valid = valid_keys(t);
     if (valid < C::BN) {
 #pragma unroll
@@ -1189,6 +1201,7 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   copies_landed_barrier();  // K(0) and Q landed, every table entry visible
 
   auto pv_only = [&](const uint8_t *vl) __attribute__((always_inline)) {
+    if (!live) return;
     bf16x8 r[3];
     r[0] = vread(vl, 0);
     r[1] = vread(vl, 1);

@@ -966,6 +966,11 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
 
   const WorkItem it = work_item(p, blockIdx.x);
   if (it.r < 0 || it.r >= p.B || it.h < 0 || it.h >= p.H) return;
+  // The first block id of an item that starts at its request's first key
+  // is entry 0 of the request's block-table row: loaded here, beside the
+  // request's lengths, instead of after them.
+  const bool first_chunk = it.chunk == 0 && p.block_table != nullptr && p.bt_stride > 0;
+  const int32_t blk0 = first_chunk ? p.block_table[(int64_t)it.r * p.bt_stride] : -1;
   const ItemRange x = item_range(p, it);
   const int head = it.h;
   const int tid = threadIdx.x;
@@ -1187,7 +1192,13 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   if (!grp_a) {
     const bool tab = cp.use_tab;
     cp.use_tab = false;
-    cp.load_ids(0, ids);
+    if (cp.whole_blocks && first_chunk) {
+      // tile 0 of whole blocks reads one block id, the one loaded above
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) ids[j] = j == 0 && cp.n_tiles_p > 0 ? blk0 : -1;
+    } else {
+      cp.load_ids(0, ids);
+    }
     pl_v = cp.plan(0, ids);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) cp.fire(pl_v, j, k0, v0);

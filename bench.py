@@ -25,10 +25,16 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_d128_config4_traffic.jso
 
 
 def kernel_source_hash():
+    """Hash of the attention kernel's code (comments and blank lines left
+    out, so that an edit of a comment keeps a traffic measurement valid)."""
+    import re
     h = hashlib.sha256()
     for f in ("attn_bf16.hip", "common.h"):
-        with open(os.path.join(ROOT, "prefix_reuse_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "prefix_reuse_attention_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 

@@ -138,7 +138,8 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   // when the suffixes are long enough to fill them, else four (128 rows).
   // At D=64 the ping-pong kernel's 64-key tiles pay when whole pool blocks
   // are copied; per-key gathers run faster in the four-wave kernel's
-  // 128-key tiles (measured: config 2 +11 % on eight waves, config 3 -8 %).
+  // 128-key tiles (measured at D=64: 64-token pages +11 % on eight waves,
+  // 4-token item blocks -8 %).
   if (const char *e = std::getenv("BAT_WAVES")) {
     pl.waves = std::atoi(e) == 8 ? 8 : 4;
   } else {

@@ -11,12 +11,14 @@
 // Crossing from the prefix tiles to the suffix tiles is the log-sum-exp
 // merge of the prefix and suffix partials, done in registers.
 //
-// Two kernels: attn_bf16_kernel, where every wave runs S^T, softmax and PV
-// of each tile in turn, and attn_bf16_pp_kernel (head dim 128, eight
-// waves), where two groups of four waves alternate between the MFMA work
-// and the softmax so that each SIMD always holds one wave of each kind.
+// Two kernels: attn_bf16_kernel (four waves), where every wave runs S^T,
+// softmax and PV of each tile in turn, and attn_bf16_pp_kernel (eight
+// waves, both head dims), where two groups of four waves alternate between
+// the MFMA work and the softmax so that each SIMD always holds one wave of
+// each kind.
 //
-// Data flow of one key tile (BN keys, 16 KB of K and 16 KB of V):
+// Data flow of one key tile (BN keys: 16 KB of K and 16 KB of V, 8 + 8 KB
+// in the eight-wave kernel at head dim 64):
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS, row-major, 16-byte
 //            chunks XOR-swizzled per row (no VGPR staging, no LDS store
 //            instructions); two LDS stages, the next tile's copy in flight

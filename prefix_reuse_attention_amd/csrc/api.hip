@@ -25,7 +25,8 @@ hipError_t launch_plan(const int32_t *cu_s, const int32_t *prefix_lens, const Pl
                        WorkItem *items, int32_t *hdr, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams &p, int D, int W, bool flat_gather, int grid,
                             hipStream_t stream);
-hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, double scale_log2,
+                           hipStream_t stream);
 hipError_t launch_merge_split(const AttnParams &p, int D, bool bf16, hipStream_t stream);
 hipError_t launch_lse_merge(const float *o_parts, const float *lse_parts, int n_parts, int rows,
                             int H, int D, bool bf16, void *out, float *lse, hipStream_t stream);
@@ -462,7 +463,9 @@ bat_status attn_rows(const void *q, const void *k, const void *v, const int32_t 
       return BAT_ERR_HIP;
   }
   const hipError_t e = dt == BAT_BF16 ? launch_attn_bf16(p, D, pl.waves, pl.flat_gather, (int)pl.grid, st)
-                                      : launch_attn_f32(p, D, (int)pl.grid, st);
+                                      : launch_attn_f32(p, D, (int)pl.grid,
+                                                        (double)softmax_scale * 1.4426950408889634074,
+                                                        st);
   if (!hip_ok(e)) return BAT_ERR_HIP;
   if (!prefix_only && pl.max_chunks > 1 && !hip_ok(launch_merge_split(p, D, dt == BAT_BF16, st)))
     return BAT_ERR_HIP;

@@ -1,5 +1,10 @@
-// Prefill attention, float32 in / float32 out, float32 arithmetic throughout
-// (true fp32 products and sums, no reduced-precision shortcuts).
+// Prefill attention, float32 in / float32 out.  The scores and the running
+// sums are taken in float64: a product of two fp32 values is exact there, so
+// each score carries one rounding, and the row sum and the output accumulator
+// over thousands of keys do not drift (summed in fp32 they miss a 1e-5
+// max-abs bar at about 1500 keys).  The exponentials take an fp32 argument,
+// s*scale*log2(e) - m formed in fp64, which is small for the terms that
+// matter, and run in fp32.
 //
 // Same semantics and work items as the bf16 kernel (Bat page, "This paper's
 // idea": cached prefix, fresh suffix that sees the prefix and itself).  This
@@ -14,8 +19,9 @@ constexpr int kF32Rows = 64;   // query rows per item
 constexpr int kF32Keys = 32;   // keys per LDS tile
 constexpr int kF32Tpr = 4;     // lanes per query row
 
+// cs: softmax_scale * log2(e) in fp64.
 template <int D>
-__global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p, double cs) {
   constexpr int DQ = D / kF32Tpr;          // dims held per lane
   constexpr int KROW = D + 4;              // LDS pitch (floats)
   __shared__ __attribute__((aligned(16))) float Ks[kF32Keys * KROW];
@@ -31,17 +37,19 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   const int row = it.m_tile * kF32Rows + rloc;
   const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
 
-  float q[DQ], o[DQ];
+  double q[DQ], o[DQ];
   {
     const float *qp = (const float *)p.q + ((int64_t)(x.q0 + row) * p.H + head) * D + part * DQ;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) {
-      q[d] = row_ok ? qp[d] : 0.f;
-      o[d] = 0.f;
+      q[d] = row_ok ? (double)qp[d] : 0.0;
+      o[d] = 0.0;
     }
   }
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  const float cs = p.scale_log2;
+  // m_run: the running max in the log2 domain, held as an fp32 value (any
+  // shift works as long as the sums and the lse use the same one)
+  float m_run = -__builtin_inff();
+  double l_run = 0.0;
 
   const int n_pkeys = x.p_end - x.p_begin;
   const int n_tiles_p = (n_pkeys + kF32Keys - 1) / kF32Keys;
@@ -82,46 +90,49 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
     }
     __syncthreads();
     // scores of this tile (every lane of a row group ends with all of them)
-    float s[kF32Keys];
-    float mx = -__builtin_inff();
+    double s[kF32Keys];
+    double mx = -__builtin_inf();
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
-      float acc = 0.f;
+      double acc = 0.0;
 #pragma unroll
-      for (int d = 0; d < DQ; ++d) acc = __builtin_fmaf(q[d], Ks[j * KROW + part * DQ + d], acc);
+      for (int d = 0; d < DQ; ++d)
+        acc = __builtin_fma(q[d], (double)Ks[j * KROW + part * DQ + d], acc);
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
-      s[j] = j < valid ? acc : -__builtin_inff();
-      mx = fmaxf(mx, s[j]);
+      s[j] = j < valid ? acc : -__builtin_inf();
+      mx = __builtin_fmax(mx, s[j]);
     }
-    const float m_new = fmaxf(m_run, mx * cs);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, (float)(mx * cs));
+    // the same alpha scales the sum and the accumulator, so its own
+    // rounding cancels in their ratio
+    const double alpha = (double)exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < DQ; ++d) o[d] *= alpha;
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < kF32Keys; ++j) {
-      const float e = exp2f(__builtin_fmaf(s[j], cs, -m_run));
+      const double e = (double)exp2f((float)(s[j] * cs - (double)m_run));
       l_run += e;
 #pragma unroll
-      for (int d = 0; d < DQ; ++d) o[d] = __builtin_fmaf(e, Vs[j * KROW + part * DQ + d], o[d]);
+      for (int d = 0; d < DQ; ++d) o[d] = __builtin_fma(e, (double)Vs[j * KROW + part * DQ + d], o[d]);
     }
   }
 
   if (!row_ok) return;
-  const float inv = 1.0f / l_run;
-  const float lse_nat = (m_run + log2f(l_run)) * 0.69314718055994530942f;
+  const double inv = 1.0 / l_run;
+  const float lse_nat = (float)(((double)m_run + log2(l_run)) * 0.69314718055994530942);
   if (!x.partial) {
     float *op = (float *)p.out + ((int64_t)(x.q0 + row) * p.H + head) * D + part * DQ;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) op[d] = o[d] * inv;
+    for (int d = 0; d < DQ; ++d) op[d] = (float)(o[d] * inv);
     if (p.lse && part == 0) p.lse[(int64_t)head * p.total_s + x.q0 + row] = lse_nat;
   } else {
     const int64_t pr = (int64_t)x.part_off + (int64_t)it.chunk * x.n_s + row;
     float *po = p.part_o + (pr * p.H + head) * D + part * DQ;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) po[d] = o[d] * inv;
+    for (int d = 0; d < DQ; ++d) po[d] = (float)(o[d] * inv);
     if (part == 0) p.part_lse[pr * p.H + head] = lse_nat;
   }
 }
@@ -129,15 +140,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
 int f32_rows_per_item() { return kF32Rows; }
 int f32_keys_per_tile() { return kF32Keys; }
 
-hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnParams &p, int D, int grid, double scale_log2,
+                           hipStream_t stream) {
   clear_stale_launch_error();
   if (grid <= 0) return hipSuccess;
   if (D == 32)
-    hipLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(256), 0, stream, p, scale_log2);
   else if (D == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(256), 0, stream, p, scale_log2);
   else if (D == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(256), 0, stream, p, scale_log2);
   else
     return hipErrorInvalidValue;
   return launch_result();

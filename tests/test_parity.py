@@ -48,6 +48,19 @@ def test_fp32_ragged(gpu_ready, D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_fp32_peaky_long_prefix(gpu_ready, D):
+    """fp32 with sharp scores (queries scaled by 4) over 2000- and 700-key
+    prefixes: outputs close to single values, thousands of terms in each row
+    sum.  The kernel takes scores and running sums in fp64; summed in fp32 in
+    key order, rows like these land at 2-3e-5 from the oracle, past the 1e-5
+    bar."""
+    wl = W.make_custom(dtype="f32", H=2, D=D, n_s=[300, 64], n_p=[2000, 700],
+                       mode=[W.USER, W.USER], seed=81, q_scale=4.0,
+                       name=f"f32_peaky_long_D{D}")
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_bf16_ragged_mixed(gpu_ready, D):
     """Several tiles and ragged tails on every axis: suffix lengths that are
     not multiples of the row tile, prefixes that end mid-block and mid-tile,

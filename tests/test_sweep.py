@@ -90,3 +90,161 @@ def test_random_batch(gpu_ready, monkeypatch, case):
     check_close(got, ref_o, wl.dtype)
     tol = 1e-5 if wl.dtype == "f32" else 1e-3
     assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"
+
+
+# ---- the other entry points, drawn the same way ---------------------------
+
+N_GQA, N_ISO, N_ROWS, N_FP8 = 8, 8, 6, 6
+
+
+def _lengths(rng, B, max_s, max_p, mode, T=1):
+    n_s = np.where(rng.random(B) < 0.2, 0, rng.integers(1, max_s, size=B)) * T
+    n_s[rng.integers(B)] = rng.integers(1, max_s) * T
+    n_p = np.where(rng.random(B) < 0.15, 0, rng.integers(1, max_p, size=B))
+    n_p = np.where(mode == W.ITEM, (n_p // W.ITEM_TOKENS) * W.ITEM_TOKENS, n_p)
+    return n_s, n_p
+
+
+def draw_gqa(case):
+    """Grouped heads: H_kv key/value heads, hg query heads each."""
+    rng = np.random.default_rng(9300 + case)
+    dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+    D = int(rng.choice([64, 128] if dtype == "bf16" else [32, 64, 128]))
+    H_kv, hg = int(rng.choice([1, 2, 4])), int(rng.choice([2, 4, 8]))
+    B = int(rng.integers(1, 5))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s, n_p = _lengths(rng, B, 520, 2000, mode)
+    env = {"BAT_WAVES": str(rng.choice(["", "4", "8"])),
+           "BAT_SPLIT_CHUNK": str(rng.choice(["", "", "512"]))}
+    wl = W.make_custom(dtype=dtype, H=H_kv, D=D, n_s=n_s, n_p=n_p, mode=mode, seed=9400 + case,
+                       user_block_size=int(rng.choice([4, 16, 64, 128])), num_items=600,
+                       name=f"sweep_gqa{case}")
+    return wl, H_kv * hg, {k: v for k, v in env.items() if v}
+
+
+def draw_isolated(case):
+    """Candidate-isolated rows: every request's suffix is whole candidates of T tokens."""
+    rng = np.random.default_rng(9500 + case)
+    dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+    D = int(rng.choice([64, 128] if dtype == "bf16" else [32, 64, 128]))
+    T = (1, 2, 4, 8)[case % 4]
+    B = int(rng.integers(1, 5))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s, n_p = _lengths(rng, B, 400 // T + 2, 2000, mode, T)
+    env = {"BAT_WAVES": str(rng.choice(["", "4", "8"]))}
+    wl = W.make_custom(dtype=dtype, H=int(rng.choice([1, 2])), D=D, n_s=n_s, n_p=n_p, mode=mode,
+                       seed=9600 + case, user_block_size=int(rng.choice([2, 16, 64])),
+                       num_items=600, q_scale=float(rng.choice([1.0, 4.0])),
+                       name=f"sweep_iso{case}")
+    return wl, T, {k: v for k, v in env.items() if v}
+
+
+def draw_prefix_rows(case):
+    """Prefix rows: each request's prefix group attends within itself."""
+    rng = np.random.default_rng(9700 + case)
+    dtype = str(rng.choice(["bf16", "f32"]))
+    D = int(rng.choice([64, 128] if dtype == "bf16" else [32, 64, 128]))
+    B = int(rng.integers(1, 6))
+    lens = np.where(rng.random(B) < 0.2, 0, rng.integers(1, 1500, size=B))
+    lens[rng.integers(B)] = rng.integers(1, 1500)
+    return dtype, D, int(rng.choice([1, 2, 3])), lens, float(rng.choice([1.0, 4.0]))
+
+
+def draw_fp8(case):
+    """E4M3 pools read back into bf16 tiles."""
+    rng = np.random.default_rng(9800 + case)
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 5))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s, n_p = _lengths(rng, B, 520, 2000, mode)
+    env = {"BAT_WAVES": str(rng.choice(["", "4", "8"])),
+           "BAT_SPLIT_CHUNK": str(rng.choice(["", "", "512"]))}
+    wl = W.make_custom(dtype="bf16", H=int(rng.choice([1, 2])), D=D, n_s=n_s, n_p=n_p, mode=mode,
+                       seed=9900 + case, user_block_size=int(rng.choice([16, 64, 128])),
+                       num_items=600, name=f"sweep_fp8_{case}")
+    return wl, {k: v for k, v in env.items() if v}
+
+
+def _set_env(monkeypatch, env):
+    for k in ("BAT_WAVES", "BAT_GATHER", "BAT_SPLIT_CHUNK"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+
+
+def test_other_draws_are_valid():
+    """Host only: every drawn case is a valid call (whole candidates per
+    request, item prefixes of whole items, at least one row), and the draws
+    reach both dtypes, every T and both workgroup shapes."""
+    seen = set()
+    for c in range(N_GQA):
+        wl, H, env = draw_gqa(c)
+        assert H % wl.H == 0 and wl.n_s.sum() > 0
+        seen.update({("gqa", wl.dtype), ("gqa_hg", H // wl.H)})
+    for c in range(N_ISO):
+        wl, T, env = draw_isolated(c)
+        assert (wl.n_s % T == 0).all() and wl.n_s.sum() > 0
+        seen.update({("iso", wl.dtype), ("T", T)})
+    for c in range(N_ROWS):
+        dtype, D, H, lens, qs = draw_prefix_rows(c)
+        assert lens.sum() > 0
+        seen.add(("rows", dtype))
+    for c in range(N_FP8):
+        wl, env = draw_fp8(c)
+        assert wl.n_s.sum() > 0
+        seen.add(("fp8", wl.D))
+    for want in [("gqa", "bf16"), ("gqa", "f32"), ("iso", "bf16"), ("iso", "f32"), ("T", 1),
+                 ("T", 2), ("T", 8), ("rows", "bf16"), ("rows", "f32"), ("fp8", 64),
+                 ("fp8", 128)]:
+        assert want in seen, want
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_GQA))
+def test_random_gqa(gpu_ready, monkeypatch, case):
+    from test_gqa import _compare as gqa_compare
+    wl, H, env = draw_gqa(case)
+    _set_env(monkeypatch, env)
+    print(f"[sweep] gqa case {case}: env={env}", flush=True)
+    gqa_compare(wl, H)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_ISO))
+def test_random_isolated(gpu_ready, monkeypatch, case):
+    from test_isolated import _compare as iso_compare
+    wl, T, env = draw_isolated(case)
+    _set_env(monkeypatch, env)
+    print(f"[sweep] isolated case {case}: env={env}", flush=True)
+    iso_compare(wl, T)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_ROWS))
+def test_random_prefix_rows(gpu_ready, case):
+    import oracle
+    from test_prefix_rows import _inputs, _prefix_rows_gpu
+    dtype, D, H, lens, q_scale = draw_prefix_rows(case)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    print(f"[sweep] prefix rows case {case}: {dtype} D={D} H={H} lens={lens.tolist()} "
+          f"q_scale={q_scale}", flush=True)
+    q, k, v = _inputs(9750 + case, int(cu[-1]), H, D, dtype, q_scale)
+    got, got_lse, scale = _prefix_rows_gpu(q, k, v, cu, dtype)
+    ref, ref_lse = oracle.prefix_rows(q, k, v, cu, scale)
+    check_close(got, ref, dtype)
+    tol = 1e-5 if dtype == "f32" else 1e-3
+    assert np.abs(got_lse - ref_lse).max() <= tol
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_FP8))
+def test_random_fp8(gpu_ready, monkeypatch, case):
+    from test_fp8 import _fp8_reference, _run_fp8
+    wl, env = draw_fp8(case)
+    _set_env(monkeypatch, env)
+    print(f"[sweep] fp8 case {case}: D={wl.D} bs={wl.user_block_size} n_s={wl.n_s.tolist()} "
+          f"n_p={wl.n_p.tolist()} mode={wl.mode.tolist()} env={env}", flush=True)
+    got, lse, _ = _run_fp8(wl)
+    ref_o, ref_l = _fp8_reference(wl)
+    check_close(got, ref_o, "bf16")
+    assert np.abs(lse - ref_l).max() <= 1e-3

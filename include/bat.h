@@ -94,7 +94,8 @@ typedef enum bat_status {
 } bat_status;
 
 typedef enum bat_dtype {
-  BAT_F32 = 0,  /* float32 in, float32 out; attention scores and sums in float64 */
+  BAT_F32 = 0,  /* float32 in/out; scores and running sums in float64 (per-item rows of
+                   at most 8 keys: float32) */
   BAT_BF16 = 1  /* bfloat16 in/out, float32 accumulation */
 } bat_dtype;
 

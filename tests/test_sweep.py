@@ -248,3 +248,55 @@ def test_random_fp8(gpu_ready, monkeypatch, case):
     ref_o, ref_l = _fp8_reference(wl)
     check_close(got, ref_o, "bf16")
     assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+# ---- many small requests ---------------------------------------------------
+
+N_WIDE = 6
+
+
+def draw_wide(case):
+    """Hundreds of short requests: the planner's item list, the per-request
+    metadata and the block-table rows at batch sizes the other draws do not
+    reach."""
+    rng = np.random.default_rng(10100 + case)
+    dtype = ("bf16", "f32")[case % 2]
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(64, 513))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s = np.where(rng.random(B) < 0.25, 0, rng.integers(1, 48, size=B))
+    n_s[rng.integers(B)] = rng.integers(1, 48)
+    n_p = np.where(rng.random(B) < 0.2, 0, rng.integers(1, 320, size=B))
+    n_p = np.where(mode == W.ITEM, (n_p // W.ITEM_TOKENS) * W.ITEM_TOKENS, n_p)
+    wl = W.make_custom(dtype=dtype, H=int(rng.choice([1, 4, 8])), D=D, n_s=n_s, n_p=n_p,
+                       mode=mode, seed=10200 + case, user_block_size=int(rng.choice([4, 16, 64])),
+                       num_items=2000, name=f"sweep_wide{case}")
+    return wl
+
+
+def test_wide_draws_are_valid():
+    """Host only: the wide draws reach both dtypes and more than 256 requests."""
+    wls = [draw_wide(c) for c in range(N_WIDE)]
+    assert {wl.dtype for wl in wls} == {"bf16", "f32"}
+    assert max(wl.B for wl in wls) > 256 and all(wl.n_s.sum() > 0 for wl in wls)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_WIDE))
+def test_random_wide_batch(gpu_ready, monkeypatch, case):
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_host
+    import torch
+    _set_env(monkeypatch, {})
+    wl = draw_wide(case)
+    print(f"[sweep] wide case {case}: dtype={wl.dtype} B={wl.B} H={wl.H} D={wl.D} "
+          f"bs={wl.user_block_size} total_s={int(wl.n_s.sum())} max_p={int(wl.n_p.max())}",
+          flush=True)
+    dw = DeviceWorkload(wl)
+    out, lse = dw.run()
+    torch.cuda.synchronize()
+    got = as_f64(to_host(out, wl.dtype), wl.dtype)
+    lse = lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oracle_full(wl)
+    check_close(got, ref_o, wl.dtype)
+    tol = 1e-5 if wl.dtype == "f32" else 1e-3
+    assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"

@@ -153,3 +153,57 @@ def test_concurrent_validated_builds_report_their_own_errors(gpu_ready, validate
         t.join()
     assert results["good"] == [api.BAT_OK] * 40
     assert results["bad"] == [api.BAT_ERR_BLOCK_TABLE] * 40
+
+
+# Every copy path of the attention kernels meets a block id outside its pool:
+# (name, dtype, head dim, user page size, BAT_WAVES, BAT_GATHER, prefix mode of
+# the request whose row is corrupted)
+BAD_ID_PATHS = [
+    ("ping_pong_d128_pages", "bf16", 128, 64, "8", "", W.USER),
+    ("ping_pong_d64_pages", "bf16", 64, 64, "8", "", W.USER),
+    ("four_wave_pages", "bf16", 128, 64, "4", "", W.USER),
+    ("four_wave_per_key", "bf16", 64, 16, "4", "", W.USER),
+    ("ping_pong_per_key", "bf16", 128, 16, "8", "", W.USER),
+    ("per_key_global_loads", "bf16", 64, 4, "4", "flat", W.USER),
+    ("ping_pong_items", "bf16", 128, 64, "8", "", W.ITEM),
+    ("fp32", "f32", 64, 16, "", "", W.USER),
+]
+
+
+@pytest.mark.parametrize("where", ["past_pool", "negative"])
+@pytest.mark.parametrize("name,dtype,D,bs,waves,gather,mode", BAD_ID_PATHS)
+def test_bad_block_id_every_copy_path(gpu_ready, monkeypatch, name, dtype, D, bs, waves, gather,
+                                      mode, where):
+    """One block id of request 0's row lies outside its pool (past the end,
+    or negative).  With validation off the call succeeds: the kernels' bounds
+    checks read that block as zeros, and request 1's rows still match the
+    oracle.  With validation on the call returns BAT_ERR_BLOCK_TABLE."""
+    import torch
+    from helpers import as_f64, check_close, oracle_full
+    from prefix_reuse_attention_amd import api
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_host
+    for k, v in (("BAT_WAVES", waves), ("BAT_GATHER", gather)):
+        if v:
+            monkeypatch.setenv(k, v)
+        else:
+            monkeypatch.delenv(k, raising=False)
+    monkeypatch.delenv("BAT_VALIDATE", raising=False)
+    wl = W.make_custom(dtype=dtype, H=2, D=D, n_s=[300, 260], n_p=[700, 512],
+                       mode=[mode, W.USER], seed=330 + D + bs, user_block_size=bs,
+                       num_items=400, name=f"bad_id_{name}")
+    dw = DeviceWorkload(wl)
+    pool_blocks = 400 if mode == W.ITEM else wl.user_num_blocks
+    bad = dw.block_table.clone()
+    bad[0, 3] = pool_blocks + 7 if where == "past_pool" else -5
+    print(f"[validate] bad block id, {name}, {where}", flush=True)
+    out, lse = dw.run(block_table=bad)
+    torch.cuda.synchronize()
+    got = as_f64(to_host(out, wl.dtype), wl.dtype)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oracle_full(wl)
+    r0, r1 = int(wl.cu_s[1]), int(wl.cu_s[2])
+    check_close(got[r0:r1], ref_o[r0:r1], wl.dtype)
+    tol = 1e-5 if dtype == "f32" else 1e-3
+    assert np.abs(got_lse[:, r0:r1] - ref_l[:, r0:r1]).max() <= tol
+    monkeypatch.setenv("BAT_VALIDATE", "1")
+    _expect_status(lambda: dw.run(block_table=bad), api.BAT_ERR_BLOCK_TABLE)

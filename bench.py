@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
-PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_FP64_TFLOPS = 78.6     # MI355X fp64 vector: the fp32 path's scores and sums are fp64 FMAs
 PEAK_HBM_GBS = 8000.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_d128_config4_traffic.json")
 
@@ -255,7 +255,7 @@ def main():
     tok_s = wl.total_s / (ms_per_step * 1e-3)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     bf16 = wl.dtype == "bf16"
-    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP64_TFLOPS
     traffic = None if (isolated or gqa_heads) else measured_traffic(wl.name, 1)
     props = torch.cuda.get_device_properties(0)
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step by wall clock, "

@@ -155,10 +155,13 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   if (const char *e = std::getenv("BAT_GATHER")) pl.flat_gather = std::strcmp(e, "flat") == 0;
   pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
   pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D, pl.waves, fp8) : f32_keys_per_tile();
-  // Split a prefix only when the unsplit batch cannot fill the GPU
-  // (about two items per CU on 256 CUs) and the prefix is long.
+  // Split a prefix only when the unsplit batch cannot fill the GPU and the
+  // prefix is long.  A CU holds two four-wave workgroups at once but one
+  // eight-wave workgroup, so the GPU is full at about 512 four-wave or 256
+  // eight-wave items on 256 CUs; splitting past that only adds partials and
+  // their merge.
   const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
-  const int64_t target = 512;
+  const int64_t target = pl.waves == 8 ? 256 : 512;
   pl.chunk_len = 0;
   if (prefix_only || !allow_split) {
     // prefix-only rows: one partial row per suffix row, no split

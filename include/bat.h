@@ -59,7 +59,7 @@
  *     every kernel form; none changes what is computed, only how):
  *       BAT_VALIDATE=1       the device checks above
  *       BAT_WAVES=4|8        bf16 rows per work item: 4 or 8 waves of 32 rows
- *                            (default: 8 when suffixes average >= 192 rows,
+ *                            (default: 8 when suffixes average > 128 rows,
  *                            else 4; also 4 at D=64 when a bfloat16 pool's
  *                            blocks hold fewer than 64 tokens, and for fp8
  *                            pools at D=128).  Workspace sizes cover either

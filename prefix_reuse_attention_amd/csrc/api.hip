@@ -136,7 +136,9 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   if (B < 0 || H <= 0 || total_s < 0 || max_s < 0 || max_p < 0) return false;
   if (!supported(dt, D)) return false;
   // bf16: eight waves (256 rows, the ping-pong kernel) share each K/V tile
-  // when the suffixes are long enough to fill them, else four (128 rows).
+  // when the suffixes average more than one four-wave item (128 rows), else
+  // four (measured at 4096-key prefixes: eight waves even at 96 and 128
+  // rows, 17-20 % ahead at 160).
   // At D=64 the ping-pong kernel's 64-key tiles pay when whole pool blocks
   // are copied; per-key gathers run faster in the four-wave kernel's
   // 128-key tiles (measured at D=64: 64-token pages +11 % on eight waves,
@@ -144,7 +146,7 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   if (const char *e = std::getenv("BAT_WAVES")) {
     pl.waves = std::atoi(e) == 8 ? 8 : 4;
   } else {
-    pl.waves = (B > 0 && (int64_t)total_s >= (int64_t)192 * B &&
+    pl.waves = (B > 0 && (int64_t)total_s > (int64_t)128 * B &&
                 !(D == 64 && per_key && !fp8)) ? 8 : 4;
   }
   // fp8 pools: the four-wave kernel at head dim 128 (the eight-wave one

@@ -8,7 +8,7 @@ again, so the cached copy has to be as good as the original wherever it
 sits.  Each case prints its name before it runs.
 
 Shapes are chosen so that the eight-wave, head-dim-128 kernel (the one
-config 4 runs) serves them: D=128 and suffixes averaging at least 192 rows.
+config 4 runs) serves them: D=128 and suffixes averaging more than 128 rows.
 """
 import numpy as np
 import pytest
@@ -46,7 +46,7 @@ def test_ping_pong_layout_independence_and_determinism(gpu_ready):
     import torch
     from prefix_reuse_attention_amd.device import DeviceWorkload
     n_s, n_p = [256, 200, 300, 256], [1000, 4096, 64, 777]
-    assert sum(n_s) >= 192 * len(n_s)
+    assert sum(n_s) > 128 * len(n_s)
     wl, wl_id = _user_pair(201, n_s, n_p)
     print(f"[bitwise] user pool D=128 n_s={n_s} n_p={n_p}", flush=True)
     a, b = DeviceWorkload(wl), DeviceWorkload(wl_id)
@@ -147,7 +147,7 @@ def test_cached_equals_recompute_ping_pong(gpu_ready):
     from prefix_reuse_attention_amd.device import DeviceWorkload
     n_s, n_p = [256, 200], [1000, 130]
     wl = W.make_custom(dtype="bf16", H=4, D=128, n_s=n_s, n_p=n_p, mode=[W.USER] * 2, seed=212)
-    assert sum(n_s) >= 192 * 2
+    assert sum(n_s) > 128 * 2
     print("[bitwise] cached = recompute, eight waves", flush=True)
     cached = DeviceWorkload(wl)
     oc, lc = cached.run(want_lse=True)

@@ -100,7 +100,7 @@ def test_isolated_single_token_fused_ping_pong(gpu_ready):
                        n_p=[700, 0, 129 * 4, 33, 64],
                        mode=[W.USER, W.USER, W.ITEM, W.USER, W.USER], seed=170,
                        num_items=300, name="iso_fused_T1")
-    assert wl.total_s >= 192 * wl.B  # the eight-wave (ping-pong) plan
+    assert wl.total_s > 128 * wl.B  # the eight-wave (ping-pong) plan
     _compare(wl, 1)
 
 

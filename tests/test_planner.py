@@ -46,8 +46,8 @@ def _check(wl, hdr, raw, H=None, hg=1):
     """H query heads (wl.H by default), hg of them per key/value head."""
     B, H = wl.B, (wl.H if H is None else H)
     total_s = int(wl.n_s.sum())
-    # eight-wave (256-row) items when suffixes average 192 rows or more
-    eight = total_s >= 192 * B
+    # eight-wave (256-row) items when suffixes average more than 128 rows
+    eight = total_s > 128 * B
     bm = 256 if eight else 128
     max_s = int(wl.n_s.max())
     t_max = -(-max_s // bm)

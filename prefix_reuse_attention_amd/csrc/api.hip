@@ -1,5 +1,6 @@
 // C ABI of libbat: argument validation, workspace layout, kernel dispatch.
 // Every launch goes on the caller's stream; nothing here allocates memory.
+#include <algorithm>
 #include <condition_variable>
 #include <cstdlib>
 #include <cstring>
@@ -161,20 +162,28 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   // prefix is long.  A CU holds two four-wave workgroups at once but one
   // eight-wave workgroup, so the GPU is full at about 512 four-wave or 256
   // eight-wave items on 256 CUs; splitting past that only adds partials and
-  // their merge.
-  const int64_t lower_items = (int64_t)H * ((total_s + pl.bm - 1) / pl.bm);
+  // their merge.  The item count is estimated from the host bounds: every
+  // request with suffix rows takes at least one row tile.  Each chunk writes
+  // an fp32 partial of its rows that the merge reads back: 2048-key chunks
+  // keep that traffic well below the chunk's compute (about 1000 flop per
+  // partial byte), 512-key ones do not, and are taken only while some CU
+  // would otherwise have no item at all.
+  const int64_t tiles_per_head =
+      std::max<int64_t>((total_s + pl.bm - 1) / pl.bm, std::min<int64_t>(B, total_s));
+  const int64_t lower_items = (int64_t)H * tiles_per_head;
   const int64_t target = pl.waves == 8 ? 256 : 512;
+  const int64_t min_chunk = lower_items >= 256 ? 2048 : 512;
   pl.chunk_len = 0;
   if (prefix_only || !allow_split) {
     // prefix-only rows: one partial row per suffix row, no split
   } else if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v > 0) pl.chunk_len = ((v + pl.bn - 1) / pl.bn) * pl.bn;
-  } else if (lower_items > 0 && lower_items < target && max_p >= 2048) {
+  } else if (lower_items > 0 && lower_items < target && max_p >= 2 * min_chunk) {
     int64_t c = (target + lower_items - 1) / lower_items;
     if (c > 64) c = 64;
     int64_t len = (max_p + c - 1) / c;
-    if (len < 512) len = 512;
+    if (len < min_chunk) len = min_chunk;
     pl.chunk_len = (int)(((len + pl.bn - 1) / pl.bn) * pl.bn);
   }
   pl.max_chunks = (pl.chunk_len > 0 && max_p > pl.chunk_len)

@@ -171,7 +171,7 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   const int64_t tiles_per_head =
       std::max<int64_t>((total_s + pl.bm - 1) / pl.bm, std::min<int64_t>(B, total_s));
   const int64_t lower_items = (int64_t)H * tiles_per_head;
-  const int64_t target = pl.waves == 8 ? 256 : 512;
+  const int64_t target = dt == BAT_BF16 && pl.waves == 8 ? 256 : 512;
   const int64_t min_chunk = lower_items >= 256 ? 2048 : 512;
   pl.chunk_len = 0;
   if (prefix_only || !allow_split) {

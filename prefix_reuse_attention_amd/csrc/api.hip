@@ -159,7 +159,7 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
   pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D, pl.waves, fp8) : f32_keys_per_tile();
   // Split a prefix only when the unsplit batch cannot fill the GPU and the
-  // prefix is long.  A CU holds two four-wave workgroups at once but one
+  // prefix is long (2048 keys or more).  A CU holds two four-wave workgroups at once but one
   // eight-wave workgroup, so the GPU is full at about 512 four-wave or 256
   // eight-wave items on 256 CUs; splitting past that only adds partials and
   // their merge.  The item count is estimated from the host bounds: every
@@ -179,7 +179,8 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   } else if (const char *e = std::getenv("BAT_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v > 0) pl.chunk_len = ((v + pl.bn - 1) / pl.bn) * pl.bn;
-  } else if (lower_items > 0 && lower_items < target && max_p >= 2 * min_chunk) {
+  } else if (lower_items > 0 && lower_items < target &&
+             max_p >= std::max<int64_t>(2048, 2 * min_chunk)) {
     int64_t c = (target + lower_items - 1) / lower_items;
     if (c > 64) c = 64;
     int64_t len = (max_p + c - 1) / c;

@@ -300,3 +300,65 @@ def test_random_wide_batch(gpu_ready, monkeypatch, case):
     check_close(got, ref_o, wl.dtype)
     tol = 1e-5 if wl.dtype == "f32" else 1e-3
     assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"
+
+
+# ---- long prefixes, few requests: the automatic prefix split ----------------
+
+N_LONG = 6
+
+
+def draw_long(case):
+    """A few requests over prefixes of up to 16k keys: too few work items to
+    fill the GPU, so the library splits the prefixes by itself (no forced
+    chunk length) and merges the partials."""
+    rng = np.random.default_rng(10300 + case)
+    dtype = ("bf16", "bf16", "f32")[case % 3]
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 4))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s = rng.integers(1, 600, size=B)
+    n_p = rng.integers(2048, 16385, size=B)
+    n_p = np.where(mode == W.ITEM, (n_p // W.ITEM_TOKENS) * W.ITEM_TOKENS, n_p)
+    wl = W.make_custom(dtype=dtype, H=int(rng.choice([1, 2])), D=D, n_s=n_s, n_p=n_p, mode=mode,
+                       seed=10400 + case, user_block_size=int(rng.choice([16, 64, 128])),
+                       num_items=5000, name=f"sweep_long{case}")
+    return wl
+
+
+def test_long_draws_split():
+    """Host only: the library's plan splits every long draw (its workspace
+    holds chunk partials, which it does not with splitting switched off)."""
+    import os
+    from prefix_reuse_attention_amd import api
+    for c in range(N_LONG):
+        wl = draw_long(c)
+        dt = api.BAT_BF16 if wl.dtype == "bf16" else api.BAT_F32
+        args = (wl.B, wl.H, wl.D, dt, int(wl.total_s), int(wl.n_s.max()), int(wl.n_p.max()))
+        split_ws = api.workspace_size(*args)
+        os.environ["BAT_SPLIT_CHUNK"] = "100000000"
+        try:
+            whole_ws = api.workspace_size(*args)
+        finally:
+            del os.environ["BAT_SPLIT_CHUNK"]
+        assert split_ws - whole_ws >= 2 * wl.total_s * wl.H * wl.D * 4, (c, split_ws, whole_ws)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_LONG))
+def test_random_long_prefixes(gpu_ready, monkeypatch, case):
+    from prefix_reuse_attention_amd.device import DeviceWorkload, to_host
+    import torch
+    _set_env(monkeypatch, {})
+    wl = draw_long(case)
+    print(f"[sweep] long case {case}: dtype={wl.dtype} B={wl.B} H={wl.H} D={wl.D} "
+          f"bs={wl.user_block_size} n_s={wl.n_s.tolist()} n_p={wl.n_p.tolist()} "
+          f"mode={wl.mode.tolist()}", flush=True)
+    dw = DeviceWorkload(wl)
+    out, lse = dw.run()
+    torch.cuda.synchronize()
+    got = as_f64(to_host(out, wl.dtype), wl.dtype)
+    lse = lse.cpu().numpy().astype(np.float64)
+    ref_o, ref_l = oracle_full(wl)
+    check_close(got, ref_o, wl.dtype)
+    tol = 1e-5 if wl.dtype == "f32" else 1e-3
+    assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"

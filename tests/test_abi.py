@@ -153,6 +153,35 @@ def test_workspace_size(lib):
     assert f(1, 2, 128, api.BAT_BF16, 64, 64, 16384) > f(1, 2, 128, api.BAT_BF16, 64, 64, 1024)
 
 
+def _partial_rows(lib, B, H, D, total_s, max_s, max_p, monkeypatch):
+    """Split-partial copies of every row in the plan: (workspace with the
+    library's policy - workspace with splitting off) / bytes of one copy."""
+    f = lib.bat_attn_workspace_size
+    split = f(B, H, D, api.BAT_BF16, total_s, max_s, max_p)
+    monkeypatch.setenv("BAT_SPLIT_CHUNK", "100000000")
+    whole = f(B, H, D, api.BAT_BF16, total_s, max_s, max_p)
+    monkeypatch.delenv("BAT_SPLIT_CHUNK")
+    return (split - whole) / (total_s * H * (D + 1) * 4)
+
+
+@pytest.mark.parametrize("B,H,n_s,n_p,chunks", [
+    (64, 8, 32, 4096, 0),     # 512 four-wave items, one per request and head: full
+    (32, 8, 128, 2048, 0),    # 256 four-wave items: a split would need 1024-key chunks
+    (16, 16, 512, 8192, 0),   # 512 eight-wave items (the 8k-history shape): full
+    (32, 8, 64, 8192, 2),     # 256 four-wave items over 8k prefixes: 4096-key chunks
+    (16, 8, 96, 8192, 4),     # 128 items: 2048-key chunks
+    (2, 16, 512, 32768, 4),   # 64 eight-wave items: 8192-key chunks, one item per CU
+    (1, 2, 64, 16384, 32),    # 2 items: 512-key chunks, the most the GPU can use
+])
+def test_split_policy(lib, monkeypatch, B, H, n_s, n_p, chunks):
+    """The automatic prefix split (D=128, equal suffixes): none when the
+    unsplit items already fill the CUs (one per request and head at least),
+    chunks of 2048 keys or more once every CU has an item, shorter ones only
+    while CUs would stay idle."""
+    got = _partial_rows(lib, B, H, 128, B * n_s, n_s, n_p, monkeypatch)
+    assert abs(got - chunks) < 0.1, (B, H, n_s, n_p, got)
+
+
 def test_prefill_workspace_size_bounds_every_call(lib):
     """The bound with the surveyed signature (no dtype, no suffix bound)
     covers the exact size for both dtypes and every suffix bound up to

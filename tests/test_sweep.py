@@ -362,3 +362,60 @@ def test_random_long_prefixes(gpu_ready, monkeypatch, case):
     check_close(got, ref_o, wl.dtype)
     tol = 1e-5 if wl.dtype == "f32" else 1e-3
     assert np.abs(lse - ref_l).max() <= tol, f"lse max-abs {np.abs(lse - ref_l).max():.3e}"
+
+
+# ---- grouped heads and fp8 pools over long prefixes (automatic split) ------
+
+N_LONG_GQA, N_LONG_FP8 = 3, 3
+
+
+def draw_long_gqa(case):
+    rng = np.random.default_rng(10500 + case)
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 4))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s = rng.integers(1, 600, size=B)
+    n_p = rng.integers(4096, 16385, size=B)
+    n_p = np.where(mode == W.ITEM, (n_p // W.ITEM_TOKENS) * W.ITEM_TOKENS, n_p)
+    H_kv = int(rng.choice([1, 2]))
+    wl = W.make_custom(dtype="bf16", H=H_kv, D=D, n_s=n_s, n_p=n_p, mode=mode,
+                       seed=10600 + case, user_block_size=64, num_items=5000,
+                       name=f"sweep_long_gqa{case}")
+    return wl, H_kv * int(rng.choice([2, 4]))
+
+
+def draw_long_fp8(case):
+    rng = np.random.default_rng(10700 + case)
+    D = (64, 128, 64)[case % 3]
+    B = int(rng.integers(1, 4))
+    mode = rng.integers(0, 2, size=B).astype(np.uint8)
+    n_s = rng.integers(1, 600, size=B)
+    n_p = rng.integers(4096, 16385, size=B)
+    n_p = np.where(mode == W.ITEM, (n_p // W.ITEM_TOKENS) * W.ITEM_TOKENS, n_p)
+    return W.make_custom(dtype="bf16", H=int(rng.choice([1, 2])), D=D, n_s=n_s, n_p=n_p,
+                         mode=mode, seed=10800 + case, user_block_size=64, num_items=5000,
+                         name=f"sweep_long_fp8_{case}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_LONG_GQA))
+def test_random_long_gqa(gpu_ready, monkeypatch, case):
+    from test_gqa import _compare as gqa_compare
+    _set_env(monkeypatch, {})
+    wl, H = draw_long_gqa(case)
+    print(f"[sweep] long gqa case {case}: H={H} H_kv={wl.H} D={wl.D}", flush=True)
+    gqa_compare(wl, H)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_LONG_FP8))
+def test_random_long_fp8(gpu_ready, monkeypatch, case):
+    from test_fp8 import _fp8_reference, _run_fp8
+    _set_env(monkeypatch, {})
+    wl = draw_long_fp8(case)
+    print(f"[sweep] long fp8 case {case}: D={wl.D} n_s={wl.n_s.tolist()} n_p={wl.n_p.tolist()} "
+          f"mode={wl.mode.tolist()}", flush=True)
+    got, lse, _ = _run_fp8(wl)
+    ref_o, ref_l = _fp8_reference(wl)
+    check_close(got, ref_o, "bf16")
+    assert np.abs(lse - ref_l).max() <= 1e-3

@@ -159,15 +159,15 @@ bool make_plan(int32_t B, int32_t H, int32_t D, bat_dtype dt, int32_t total_s, i
   pl.bm = dt == BAT_BF16 ? bf16_rows_per_item(pl.waves) : f32_rows_per_item();
   pl.bn = dt == BAT_BF16 ? bf16_keys_per_tile(D, pl.waves, fp8) : f32_keys_per_tile();
   // Split a prefix only when the unsplit batch cannot fill the GPU and the
-  // prefix is long (2048 keys or more).  A CU holds two four-wave workgroups at once but one
-  // eight-wave workgroup, so the GPU is full at about 512 four-wave or 256
-  // eight-wave items on 256 CUs; splitting past that only adds partials and
-  // their merge.  The item count is estimated from the host bounds: every
-  // request with suffix rows takes at least one row tile.  Each chunk writes
-  // an fp32 partial of its rows that the merge reads back: 2048-key chunks
-  // keep that traffic well below the chunk's compute (about 1000 flop per
-  // partial byte), 512-key ones do not, and are taken only while some CU
-  // would otherwise have no item at all.
+  // prefix is long (2048 keys or more).  A CU holds two four-wave
+  // workgroups at once but one eight-wave workgroup, so the GPU is full at
+  // about 512 four-wave or 256 eight-wave items on 256 CUs; splitting past
+  // that only adds partials and their merge.  The item count is estimated
+  // from the host bounds: every request with suffix rows takes at least one
+  // row tile.  Each chunk writes an fp32 partial of its rows that the merge
+  // reads back: 2048-key chunks keep that traffic well below the chunk's
+  // compute (about 1000 flop per partial byte), 512-key ones do not, and are
+  // taken only while some CU would otherwise have no item at all.
   const int64_t tiles_per_head =
       std::max<int64_t>((total_s + pl.bm - 1) / pl.bm, std::min<int64_t>(B, total_s));
   const int64_t lower_items = (int64_t)H * tiles_per_head;

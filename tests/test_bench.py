@@ -1,0 +1,47 @@
+"""Host checks of bench.py's contract (no GPU): more than one GPU is refused
+before anything touches a device, and the committed HBM-traffic summary
+belongs to the attention kernel's current source, so that the bench line's
+`roofline.traffic` is a measurement of the code that runs."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_summary_matches_the_kernel_source():
+    with open(bench.PMC_SUMMARY) as f:
+        s = json.load(f)
+    assert s["kernel_source_hash"] == bench.kernel_source_hash()
+    got = bench.measured_traffic(s["config"], 1)
+    assert got is not None and got > 0
+    # the traffic is the algorithmic bytes of config 4 within a few percent
+    alg = ((2 * 8192 + 4 * 512) * 128 * 2 + 4 * 512) * 16 * 16
+    assert abs(got / alg - 1.0) < 0.05
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    """The hash covers code only: a comment or blank line edit keeps it."""
+    csrc = tmp_path / "prefix_reuse_attention_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("attn_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "prefix_reuse_attention_amd", "csrc", f)) as fh:
+            (csrc / f).write_text(fh.read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    (csrc / "common.h").write_text((csrc / "common.h").read_text() + "\n// a note\n\n/* more */\n")
+    assert bench.kernel_source_hash() == h0
+    (csrc / "common.h").write_text((csrc / "common.h").read_text() + "\nconstexpr int kX = 1;\n")
+    assert bench.kernel_source_hash() != h0

@@ -21,7 +21,15 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP64_TFLOPS = 78.6     # MI355X fp64 vector: the fp32 path's scores and sums are fp64 FMAs
 PEAK_HBM_GBS = 8000.0
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_d128_config4_traffic.json")
+# committed HBM-traffic summaries (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), one per
+# configuration, each with the hash of the kernel source it was measured on
+PMC_SUMMARIES = {
+    "config2": os.path.join(ROOT, "profiles", "attn_bf16_d64_config2_traffic.json"),
+    "config3": os.path.join(ROOT, "profiles", "attn_bf16_d64_config3_traffic.json"),
+    "config4": os.path.join(ROOT, "profiles", "attn_bf16_d128_config4_traffic.json"),
+    "config5": os.path.join(ROOT, "profiles", "attn_bf16_d128_config5_traffic.json"),
+}
+PMC_SUMMARY = PMC_SUMMARIES["config4"]
 
 
 def kernel_source_hash():
@@ -41,8 +49,11 @@ def kernel_source_hash():
 def measured_traffic(config, per_launch_units):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
     None when the kernel source changed since the counters were taken."""
+    path = PMC_SUMMARIES.get(config)
+    if path is None:
+        return None
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(path) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
@@ -68,16 +79,21 @@ def _pmc_kib(run_dir, counter, name_part):
 
 
 def bf16_kernel_label(wl):
-    """The bf16 kernel the library launches for this workload: eight waves
-    (256 rows per item) when suffixes average at least 192 rows (and, at
-    D=64, the longest prefix has at least 4096 keys), else four;
-    with eight waves and head dim 128 the ping-pong kernel.  Buffer-load
-    copies (the global-load form only serves per-key pools of 2 GiB or
-    more)."""
-    waves = 8 if wl.total_s >= 192 * wl.B and (wl.D == 128 or int(wl.n_p.max()) >= 4096) else 4
-    if waves == 8 and wl.D == 128:
-        return "attn_bf16_pp_kernel<128, false>"
-    return f"attn_bf16_kernel<{wl.D}, {waves}, false>"
+    """The bf16 kernel the library launches for this workload, by the same
+    rule as its planner: the eight-wave ping-pong kernel (256 rows per item,
+    64-key tiles) when suffixes average more than 128 rows, except at D=64
+    over a pool whose blocks are smaller than a 64-key tile (gathered key
+    by key, faster on four waves); else the four-wave kernel.  Buffer-load
+    copies: the global-load form only serves per-key pools of 2 GiB or
+    more, and none of these workloads has one."""
+    from prefix_reuse_attention_amd import workloads as W
+    has_user = bool((wl.mode == W.USER).any())
+    has_item = bool((wl.mode == W.ITEM).any())
+    per_key = (has_user and wl.user_block_size < 64) or (has_item and W.ITEM_TOKENS < 64)
+    eight = wl.total_s > 128 * wl.B and not (wl.D == 64 and per_key)
+    if eight:
+        return f"attn_bf16_pp_kernel<{wl.D}, false>"
+    return f"attn_bf16_kernel<{wl.D}, 4, false>"
 
 
 def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
@@ -94,7 +110,9 @@ def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
                "kernel_source_hash": kernel_source_hash(),
                "fetch_kib": f, "write_kib": w, "fetch_scale": f_scale, "write_scale": w_scale,
                "hbm_bytes_per_launch": (f * f_scale + w * w_scale) * 1024.0}
-    with open(PMC_SUMMARY, "w") as fh:
+    if config not in PMC_SUMMARIES:
+        raise SystemExit(f"no traffic summary file is kept for {config}")
+    with open(PMC_SUMMARIES[config], "w") as fh:
         json.dump(summary, fh, indent=1)
         fh.write("\n")
     print(json.dumps(summary), flush=True)
@@ -245,6 +263,7 @@ def main():
         step = dw.prepared(out, lse, ws)  # arguments marshalled once
 
     ms_per_step, kernel_ms = _timed_steps(step, args.steps, args.warmup, stream)
+    per_call = _per_call_ms(step, args.steps, stream)
     flops = wl.flops()
     alg_bytes = wl.alg_bytes()
     if gqa_heads:  # the work of the query heads
@@ -299,6 +318,7 @@ def main():
                                + ((" (own key folded in)" if bf16
                                    else " + item_local_kernel (merge)") if isolated else ""),
                      "kernel_ms_mean": round(kernel_ms, 5)},
+        "per_call_ms": per_call,
         "kv_build": {"ms": round(build_ms, 4), "bytes_copied": build_bytes,
                      "GB_per_s_read_plus_write": round(2 * build_bytes / (build_ms * 1e-3) / 1e9, 1),
                      "note": "once per prefix; amortised over every query that reuses it"},
@@ -484,6 +504,28 @@ def _timed_steps(step, steps, warmup, stream):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     return wall_ms, start.elapsed_time(end) / steps
+
+
+def _per_call_ms(step, calls, stream):
+    """Distribution of single calls, in a pass of its own after the timed
+    steps: each call between its own pair of HIP events on the kernels'
+    stream (events between calls would slow the timed region itself).
+    Returns {median, min, p90, calls} in ms, or None for no calls."""
+    import numpy as np
+    import torch
+    if calls <= 0:
+        return None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"median": round(float(np.median(ms)), 5), "min": round(float(ms.min()), 5),
+            "p90": round(float(np.percentile(ms, 90)), 5), "calls": calls,
+            "note": "per-call HIP events, in an untimed pass of as many calls after the timed steps"}
 
 
 def bench_prefix_workload(args):

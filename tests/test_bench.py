@@ -4,8 +4,11 @@ belongs to the attention kernel's current source, so that the bench line's
 `roofline.traffic` is a measurement of the code that runs."""
 import json
 import os
+import re
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -30,6 +33,39 @@ def test_traffic_summary_matches_the_kernel_source():
     # the traffic is the algorithmic bytes of config 4 within a few percent
     alg = ((2 * 8192 + 4 * 512) * 128 * 2 + 4 * 512) * 16 * 16
     assert abs(got / alg - 1.0) < 0.05
+
+
+def test_every_committed_traffic_summary_is_current():
+    """Each per-configuration summary that is committed names its own
+    configuration and the kernel source that runs now."""
+    found = 0
+    for config, path in bench.PMC_SUMMARIES.items():
+        if not os.path.exists(path):
+            continue
+        found += 1
+        with open(path) as f:
+            s = json.load(f)
+        assert s["config"] == config
+        assert s["kernel_source_hash"] == bench.kernel_source_hash()
+        assert bench.measured_traffic(config, 1) == s["hbm_bytes_per_launch"] > 0
+    assert found >= 1
+    assert bench.measured_traffic("config9", 1) is None
+
+
+@pytest.mark.parametrize("config,profile", [
+    (2, "attn_bf16_d64_config2.md"), (3, "attn_bf16_d64_config3.md"),
+    (4, "attn_bf16_d128_config4.md"), (5, "attn_bf16_d128_config5.md")])
+def test_kernel_label_is_the_kernel_the_profile_traced(config, profile):
+    """The bench line's kernel name follows the library's workgroup-shape
+    rule; the committed kernel trace of each configuration shows which
+    kernel the library actually launched."""
+    from prefix_reuse_attention_amd import workloads as W
+    with open(os.path.join(ROOT, "profiles", profile)) as f:
+        traced = re.findall(r'^"void bat::(attn_bf16_\w+<[^>]*>)\(', f.read(), flags=re.M)
+    assert len(set(traced)) == 1
+    label = bench.bf16_kernel_label(W.make_config(config))
+    # the trace names every template argument, the label the first ones
+    assert traced[0].startswith(label[:-1])
 
 
 def test_source_hash_ignores_comments(tmp_path, monkeypatch):

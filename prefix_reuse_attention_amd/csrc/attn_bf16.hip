@@ -982,13 +982,23 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   const int col = lane & 31, hf = lane >> 5;
   const bool grp_a = wave < 4;
 
-  const int row = it.m_tile * BM + wave * 32 + col;
+  // The 32-row block a wave owns.  In the first row tile of a request it is
+  // the wave's index.  In later tiles the blocks alternate between the groups
+  // (0, 4, 1, 5, ...), so that a short last tile keeps live waves in both
+  // groups: its steps then take as long as those of the request's full
+  // tiles, which read the same prefix tiles at the same time through L2.
+  // With group A alone it would run ahead of them (a phase without the
+  // other group's contention is shorter), and once its lead passed what L2
+  // holds, the full tiles would fetch the prefix from memory again.  A
+  // request with one row tile has no such partner and keeps the plain order.
+  const int blk_rows = it.m_tile > 0 ? ((wave & 3) * 2 + (wave >> 2)) : wave;
+  const int row = it.m_tile * BM + blk_rows * 32 + col;
   // A wave whose 32 rows all lie past the suffix's end (the last row tile
   // of a suffix that is not a multiple of 256 rows) computes nothing: it
   // skips its operand reads, MFMAs and softmax, and keeps only its part in
   // the barriers and, in group B, in the copies.
   const bool live =
-      __builtin_amdgcn_readfirstlane((int)(it.m_tile * BM + wave * 32 < x.n_s)) != 0;
+      __builtin_amdgcn_readfirstlane((int)(it.m_tile * BM + blk_rows * 32 < x.n_s)) != 0;
   const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
   bf16x8 qf[C::KK];
 

@@ -159,6 +159,20 @@ def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_bf16_later_row_tiles_every_live_block_count(gpu_ready, monkeypatch, D):
+    """Eight-wave items past a request's first row tile give their 32-row
+    blocks to the two wave groups in turn.  Suffixes whose later tiles hold
+    1, 32, 44, 128, 144, 255, 256 and 257 rows (one to eight live blocks,
+    full and ragged) must still cover every row exactly once."""
+    monkeypatch.setenv("BAT_WAVES", "8")
+    n_s = [257, 288, 300, 384, 400, 511, 512, 769]
+    n_p = [130, 0, 64, 200, 1000, 77, 256, 300]
+    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s, n_p=n_p, mode=[W.USER] * 8,
+                       seed=190 + D, user_block_size=64, name=f"bf16_later_tiles_D{D}")
+    _compare_full(wl)
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_bf16_tile_counts(gpu_ready, monkeypatch, D):
     """Items of 1 to 6 key tiles with eight waves per workgroup (the
     ping-pong kernel alternates two wave groups over a two-phase step, with

@@ -982,24 +982,38 @@ __global__ __launch_bounds__(512, 2) void attn_bf16_pp_kernel(AttnParams p) {
   const int col = lane & 31, hf = lane >> 5;
   const bool grp_a = wave < 4;
 
-  // The 32-row block a wave owns.  In the first row tile of a request it is
-  // the wave's index.  In later tiles the blocks alternate between the groups
-  // (0, 4, 1, 5, ...), so that a short last tile keeps live waves in both
-  // groups: its steps then take as long as those of the request's full
-  // tiles, which read the same prefix tiles at the same time through L2.
-  // With group A alone it would run ahead of them (a phase without the
-  // other group's contention is shorter), and once its lead passed what L2
-  // holds, the full tiles would fetch the prefix from memory again.  A
-  // request with one row tile has no such partner and keeps the plain order.
-  const int blk_rows = it.m_tile > 0 ? ((wave & 3) * 2 + (wave >> 2)) : wave;
-  const int row = it.m_tile * BM + blk_rows * 32 + col;
-  // A wave whose 32 rows all lie past the suffix's end (the last row tile
-  // of a suffix that is not a multiple of 256 rows) computes nothing: it
-  // skips its operand reads, MFMAs and softmax, and keeps only its part in
-  // the barriers and, in group B, in the copies.
-  const bool live =
-      __builtin_amdgcn_readfirstlane((int)(it.m_tile * BM + blk_rows * 32 < x.n_s)) != 0;
-  const bool row_ok = row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
+  // The rows of this item.  A request of n_s rows has ceil(n_s / 256) row
+  // tiles (as planned), and its 32-row blocks are dealt over them evenly
+  // (counts differing by at most one), not 256 rows at a time with the rest
+  // left to the last tile.  Inside a tile of a multi-tile request the
+  // blocks alternate between the groups (waves 0, 4, 1, 5, ...), so that
+  // every tile keeps live waves in both groups.  The tiles of a request
+  // then take about equally long per step and read the same prefix tiles at
+  // about the same time, through L2; a short tile on group A alone ran
+  // ahead of its full partners, which then fetched the prefix from memory
+  // again once its lead passed what L2 holds.  A single-tile request has no
+  // partner and keeps the plain order (a short one stays on group A, where
+  // its steps cost less).
+  int blk_first = 0, blk_count = 8, blk_rows = wave;
+  {
+    const int n_tiles_r = (x.n_s + BM - 1) / BM;
+    if (n_tiles_r > 1) {
+      const int nblk = (x.n_s + 31) >> 5;
+      const int q = nblk / n_tiles_r, rem = nblk - q * n_tiles_r;
+      blk_first = it.m_tile * q + min(it.m_tile, rem);
+      blk_count = q + (it.m_tile < rem ? 1 : 0);
+      blk_rows = (wave & 3) * 2 + (wave >> 2);
+    }
+  }
+  const bool in_tile = blk_rows < blk_count;
+  const int row = (blk_first + blk_rows) * 32 + col;
+  // A wave whose 32 rows all lie outside the item (past the suffix's end, or
+  // in a block the tile does not hold) computes nothing: it skips its
+  // operand reads, MFMAs and softmax, and keeps only its part in the
+  // barriers and, in group B, in the copies.
+  const bool live = __builtin_amdgcn_readfirstlane(
+                        (int)(in_tile && (blk_first + blk_rows) * 32 < x.n_s)) != 0;
+  const bool row_ok = in_tile && row < x.n_s && x.q0 >= 0 && x.q0 + row < p.total_s;
   bf16x8 qf[C::KK];
 
   TC cp;

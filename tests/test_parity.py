@@ -159,16 +159,18 @@ def test_bf16_workgroup_shapes(gpu_ready, monkeypatch, waves, D):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_bf16_later_row_tiles_every_live_block_count(gpu_ready, monkeypatch, D):
-    """Eight-wave items past a request's first row tile give their 32-row
-    blocks to the two wave groups in turn.  Suffixes whose later tiles hold
-    1, 32, 44, 128, 144, 255, 256 and 257 rows (one to eight live blocks,
-    full and ragged) must still cover every row exactly once."""
+def test_bf16_row_blocks_dealt_over_row_tiles(gpu_ready, monkeypatch, D):
+    """Eight-wave items: a request's 32-row blocks are dealt evenly over its
+    256-row tiles and, when it has more than one, alternate between the two
+    wave groups inside each tile.  Requests of 257 to 769 rows give tiles of
+    four to eight blocks with a partial last block (1, 12, 16, 24 or 31 rows) or
+    none, and requests of one tile (1 and 100 rows) keep the plain order.
+    Every row must be computed once, by the right wave, against the oracle."""
     monkeypatch.setenv("BAT_WAVES", "8")
-    n_s = [257, 288, 300, 384, 400, 511, 512, 769]
-    n_p = [130, 0, 64, 200, 1000, 77, 256, 300]
-    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s, n_p=n_p, mode=[W.USER] * 8,
-                       seed=190 + D, user_block_size=64, name=f"bf16_later_tiles_D{D}")
+    n_s = [257, 288, 300, 384, 400, 511, 512, 600, 769, 1, 100]
+    n_p = [130, 0, 64, 200, 1000, 77, 256, 70, 300, 500, 64]
+    wl = W.make_custom(dtype="bf16", H=2, D=D, n_s=n_s, n_p=n_p, mode=[W.USER] * len(n_s),
+                       seed=190 + D, user_block_size=64, name=f"bf16_row_blocks_D{D}")
     _compare_full(wl)
 
 

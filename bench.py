@@ -80,7 +80,7 @@ def _pmc_kib(run_dir, counter, name_part):
 
 def bf16_kernel_label(wl):
     """The bf16 kernel the library launches for this workload, by the same
-    rule as its planner: the eight-wave ping-pong kernel (256 rows per item,
+    rule as its planner: the eight-wave ping-pong kernel (up to 256 rows per item,
     64-key tiles) when suffixes average more than 128 rows, except at D=64
     over a pool whose blocks are smaller than a 64-key tile (gathered key
     by key, faster on four waves); else the four-wave kernel.  Buffer-load
@@ -388,7 +388,8 @@ def bench_fp8_workload(args):
             "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel": f"attn_bf16_kernel<{wl.D}, 4, false, true>",
+                         "kernel": "attn_bf16_kernel<{}, {}, false, true>".format(
+                             wl.D, 8 if wl.D == 64 and wl.total_s > 128 * wl.B else 4),
                          "kernel_ms_mean": round(kernel_ms, 5)}}
     print(json.dumps(line), flush=True)
 

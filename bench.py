@@ -96,6 +96,47 @@ def bf16_kernel_label(wl):
     return f"attn_bf16_kernel<{wl.D}, 4, false>"
 
 
+def batch_from_spec(spec):
+    """A seeded synthetic batch from a spec of comma-separated key=value
+    pairs: B, H, D (bf16), n_p and n_s (an integer, or lo:hi for lengths
+    drawn uniformly from [lo, hi]), mode (user, item or mixed: each request
+    user or item with probability one half; item prefixes are rounded down
+    to whole 4-token items) and seed.  Example: "B=128,H=8,D=128,n_p=8192,
+    n_s=257:512".  The lengths come from numpy's default generator with that
+    seed, the tensors from the workload generator with it."""
+    import numpy as np
+    from prefix_reuse_attention_amd import workloads as W
+    kv = dict(item.split("=", 1) for item in spec.split(",") if item)
+    unknown = set(kv) - {"B", "H", "D", "n_p", "n_s", "mode", "seed"}
+    if unknown:
+        raise SystemExit(f"--batch: unknown keys {sorted(unknown)}")
+    B, H, D = int(kv.get("B", 16)), int(kv.get("H", 8)), int(kv.get("D", 128))
+    seed = int(kv.get("seed", 11))
+    rng = np.random.default_rng(seed)
+
+    def lengths(text):
+        if ":" in text:
+            lo, hi = (int(x) for x in text.split(":"))
+            return rng.integers(lo, hi + 1, B)
+        return np.full(B, int(text))
+    n_p, n_s = lengths(kv.get("n_p", "8192")), lengths(kv.get("n_s", "512"))
+    how = kv.get("mode", "user")
+    if how == "user":
+        mode = np.full(B, W.USER)
+    elif how == "item":
+        mode = np.full(B, W.ITEM)
+    elif how == "mixed":
+        mode = np.where(rng.random(B) < 0.5, W.ITEM, W.USER)
+    else:
+        raise SystemExit(f"--batch: mode must be user, item or mixed, not {how}")
+    n_p = np.where(mode == W.ITEM, W.ITEM_TOKENS * (n_p // W.ITEM_TOKENS), n_p)
+    wl = W.make_custom(dtype="bf16", H=H, D=D, n_s=n_s.tolist(), n_p=n_p.tolist(),
+                       mode=mode.tolist(), seed=seed, user_block_size=64,
+                       name="batch:" + spec)
+    wl.notes["description"] = f"synthetic batch {spec}"
+    return wl
+
+
 def write_traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of the
     benchmark and of --copy-calibration) into the HBM-traffic summary that
@@ -140,6 +181,10 @@ def main():
                          "the planner splits into chunks merged by log-sum-exp; fp8: "
                          "bat_attn_prefill_fp8 on --config with the prefix pool in fp8 "
                          "(bat_kv_build_fp8)")
+    ap.add_argument("--batch", default=None,
+                    help="with the default workload: time a synthetic batch given by its sizes "
+                         "instead of --config (e.g. B=128,H=8,D=128,n_p=8192,n_s=257:512,"
+                         "mode=user); see batch_from_spec")
     ap.add_argument("--host-sweep", action="store_true",
                     help="with --workload schedule: only the host accounting of both policies "
                          "over a grid of traffic shapes (no GPU needed)")
@@ -209,6 +254,8 @@ def main():
                            mode=[W.USER] * 2, seed=105, user_block_size=64, name="split_32k")
         wl.notes["description"] = ("bf16, B=2, H=16, D=128, user prefix 32768 (64-token pages), "
                                    "suffix 512; prefixes split into chunks")
+    elif args.batch:
+        wl = batch_from_spec(args.batch)
     else:
         wl = W.make_config(args.config)
     print(f"[bench] generated {wl.name} in {time.time() - t0:.1f}s: {wl.notes['description']}",

@@ -81,3 +81,24 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     (csrc / "common.h").write_text((csrc / "common.h").read_text() + "\nconstexpr int kX = 1;\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_batch_spec():
+    """--batch builds the batch its spec names: fixed or uniformly drawn
+    lengths within their bounds, item prefixes in whole 4-token items, the
+    same batch for the same seed, and an error for an unknown key."""
+    from prefix_reuse_attention_amd import workloads as W
+    wl = bench.batch_from_spec("B=6,H=2,D=64,n_p=100:900,n_s=257:512,mode=mixed,seed=5")
+    assert (wl.B, wl.H, wl.D) == (6, 2, 64)
+    assert ((wl.n_s >= 257) & (wl.n_s <= 512)).all()
+    assert ((wl.n_p >= 96) & (wl.n_p <= 900)).all()
+    assert (wl.n_p[wl.mode == W.ITEM] % W.ITEM_TOKENS == 0).all()
+    again = bench.batch_from_spec("B=6,H=2,D=64,n_p=100:900,n_s=257:512,mode=mixed,seed=5")
+    assert (again.n_s == wl.n_s).all() and (again.n_p == wl.n_p).all()
+    assert (again.mode == wl.mode).all()
+    fixed = bench.batch_from_spec("B=3,H=1,D=128,n_p=8192,n_s=300")
+    assert fixed.n_p.tolist() == [8192] * 3 and fixed.n_s.tolist() == [300] * 3
+    assert (fixed.mode == W.USER).all()
+    assert bench.measured_traffic(fixed.name, 1) is None
+    with pytest.raises(SystemExit):
+        bench.batch_from_spec("B=3,rows=4")

@@ -1,7 +1,10 @@
-"""Host checks of bench.py's contract (no GPU): more than one GPU is refused
-before anything touches a device, and the committed HBM-traffic summary
-belongs to the attention kernel's current source, so that the bench line's
-`roofline.traffic` is a measurement of the code that runs."""
+"""Checks of bench.py's contract.  On the host: more than one GPU is refused
+before anything touches a device, the committed HBM-traffic summaries belong
+to the attention kernel's current source (so that the bench line's
+`roofline.traffic` is a measurement of the code that runs), the kernel label
+follows the planner's rule, and --batch builds the batch its spec names.  On
+the GPU: bench.py end to end on small workloads prints one line with the
+contract's fields."""
 import json
 import os
 import re
@@ -102,3 +105,35 @@ def test_batch_spec():
     assert bench.measured_traffic(fixed.name, 1) is None
     with pytest.raises(SystemExit):
         bench.batch_from_spec("B=3,rows=4")
+
+
+def _bench_line(*args):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("args,kernel", [
+    (("--config", "1"), "attn_f32_kernel<32>"),
+    (("--batch", "B=2,H=2,D=128,n_p=200,n_s=300"), "attn_bf16_pp_kernel<128, false>"),
+    (("--batch", "B=3,H=2,D=64,n_p=64:400,n_s=20:90,mode=mixed,seed=4"),
+     "attn_bf16_kernel<64, 4, false>")])
+def test_bench_line_on_the_gpu(gpu_ready, args, kernel):
+    """bench.py end to end on small workloads: one JSON line with the
+    contract's fields, the timed steps and the per-call pass, and the kernel
+    the planner's rule names."""
+    d = _bench_line(*args, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["roofline"]["kernel"] == kernel
+    assert d["roofline"]["achieved"] > 0 and 0 <= d["roofline"]["frac"] < 1
+    pc = d["per_call_ms"]
+    assert pc["calls"] == 3 and 0 < pc["min"] <= pc["median"] <= pc["p90"]

@@ -106,7 +106,10 @@ def batch_from_spec(spec):
     seed, the tensors from the workload generator with it."""
     import numpy as np
     from prefix_reuse_attention_amd import workloads as W
-    kv = dict(item.split("=", 1) for item in spec.split(",") if item)
+    items = [item for item in spec.split(",") if item]
+    if any("=" not in item for item in items):
+        raise SystemExit(f"--batch: expected key=value pairs, got {spec!r}")
+    kv = dict(item.split("=", 1) for item in items)
     unknown = set(kv) - {"B", "H", "D", "n_p", "n_s", "mode", "seed"}
     if unknown:
         raise SystemExit(f"--batch: unknown keys {sorted(unknown)}")

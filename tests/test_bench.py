@@ -105,6 +105,8 @@ def test_batch_spec():
     assert bench.measured_traffic(fixed.name, 1) is None
     with pytest.raises(SystemExit):
         bench.batch_from_spec("B=3,rows=4")
+    with pytest.raises(SystemExit):
+        bench.batch_from_spec("B=3,D128")
 
 
 def _bench_line(*args):
